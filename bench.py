@@ -1,0 +1,353 @@
+#!/usr/bin/env python3
+"""Benchmark of the Stem sparse-prefill path on one MI355X.
+
+One step = one attention layer of Stem prefill: block scoring (value-norm
+bonus + strided anti-diagonal score GEMM), the token-position-decay schedule
+with per-row top-k, and causal block-sparse attention over the lists.  The
+default workload is the 128K-token Qwen3-8B-shaped layer (32 query heads, 8
+KV heads, d = 128) at ~25 % kept block pairs, timed against the library's own
+dense causal attention on the same inputs.
+
+    python bench.py [--steps K] [--warmup W] [--no-sweep] [--no-cpu-baseline]
+    python bench.py --fp8        # 36-layer fp8 varlen schedule instead
+
+Prints ONE JSON line.  value = effective TFLOP/s = dense-equivalent causal
+attention FLOP (4 d Hq sum_z L_z (L_z + 1) / 2) / Stem end-to-end time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms/layer + effective TFLOP/s, Stem prefill @128K, 25% density vs own dense"
+PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16/fp16 MFMA
+PEAK_FP8_TFLOPS = 5000.0        # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def dense_flop(seqlens, Hq, d=128):
+    return 4.0 * d * Hq * sum(L * (L + 1) / 2 for L in seqlens)
+
+
+def bsa_pairs(idx, cnt, p):
+    """Computed (query, key) token pairs of the lists; the diagonal block counts 128*129/2."""
+    import torch
+    rows = torch.arange(p.R, device=cnt.device)
+    starts = torch.tensor(p.cu[:-1], device=cnt.device) // 128
+    seq_of = torch.repeat_interleave(torch.arange(len(p.nbs), device=cnt.device),
+                                     torch.tensor(p.nbs, device=cnt.device))
+    I = rows - starts[seq_of]
+    last = torch.gather(idx, 2, (cnt.clamp(min=1) - 1).long().unsqueeze(-1)).squeeze(-1)
+    has_diag = (cnt > 0) & (last == I.unsqueeze(0))
+    full = cnt.to(torch.int64) - has_diag.to(torch.int64)
+    return int((full * 16384 + has_diag.to(torch.int64) * 8256).sum().item())
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "block_sparse_attention_stem_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, sha):
+    """HBM bytes per launch measured by rocprofv3 --pmc, if taken on this exact source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("source_sha") != sha:
+        return None
+    return t.get("bytes_per_launch")
+
+
+class StageTimer:
+    """HIP events on the stream the library launches on (torch's current stream)."""
+
+    def __init__(self, torch, names):
+        self.torch, self.names = torch, names
+        self.samples = {n: [] for n in names}
+
+    def run(self, fns):
+        ev = [self.torch.cuda.Event(enable_timing=True) for _ in range(len(fns) + 1)]
+        ev[0].record()
+        for i, fn in enumerate(fns):
+            fn()
+            ev[i + 1].record()
+        return ev
+
+    def collect(self, ev):
+        for i, n in enumerate(self.names):
+            self.samples[n].append(ev[i].elapsed_time(ev[i + 1]))
+
+    def mean(self, n):
+        s = self.samples[n]
+        return sum(s) / len(s)
+
+
+def cpu_baseline(w, q, k, v, idx, cnt, gpu_flop_dense, budget_s=20.0):
+    """Time the oracle on a bounded sample of the same workload and scale by work."""
+    import numpy as np
+    import torch
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    L = w.seqlens[0]
+    nb = L // 128
+    Hq, Hkv = w.num_q_heads, w.num_kv_heads
+    G = Hq // Hkv
+    d = 128
+    sc = 1.0 / math.sqrt(d)
+    parts = []
+    # --- score: head 0, the first query chunks (causal cost grows with the chunk index)
+    t0 = time.perf_counter()
+    vf = v[:, 0:1, :].to(torch.float64).numpy()
+    bon = O.value_bonus(vf, [0, L], 128, w.beta)
+    t_vn = time.perf_counter() - t0
+    qf = q[:, 0:1, :].to(torch.float64).numpy()
+    kf = k[:, 0:1, :].to(torch.float64).numpy()
+    done_pairs, t_sc, c = 0, 0.0, 0
+    scale = 1.0 / (math.sqrt(d) * w.stride * w.norm)
+    while t_sc < budget_s * 0.4 and c * w.chunk_size < L:
+        c0, c1 = c * w.chunk_size, min((c + 1) * w.chunk_size, L)
+        t0 = time.perf_counter()
+        A = O.strided_scores(qf[:, 0], kf[:, 0], w.stride, scale, c0 // w.stride, c1 // w.stride)
+        m = 128 // w.stride
+        A.reshape((c1 - c0) // 128, m, A.shape[1] // m, m).max(axis=(1, 3))
+        t_sc += time.perf_counter() - t0
+        I0, I1 = c0 // 128, c1 // 128
+        done_pairs += sum(I + 1 for I in range(I0, I1))
+        c += 1
+    total_pairs = Hq * nb * (nb + 1) / 2
+    est_score = t_sc * total_pairs / done_pairs + t_vn * Hkv
+    parts.append(f"score: head 0, {c} chunk(s) of {w.chunk_size} ({done_pairs} of {int(total_pairs)} "
+                 f"block pairs), v-bonus of 1 of {Hkv} KV heads")
+    # --- schedule: 512 rows of head 0 on the GPU's scores are not needed: any
+    # fp32 scores exercise the same work; use random ones of the right shape.
+    rng = np.random.default_rng(0)
+    rows = list(range(nb - 256, nb))
+    t0 = time.perf_counter()
+    for I in rows:
+        row = rng.standard_normal(I + 1).astype(np.float32)
+        kept = O.kept_count(I, nb, w.k_start[0], w.mu, w.alpha, w.n_init, w.n_window)
+        O.select_row(row, I, kept, O.forced_blocks(I, w.n_init, w.n_window))
+    t_tk = time.perf_counter() - t0
+    est_topk = t_tk * (Hq * nb) / len(rows)
+    parts.append(f"schedule: {len(rows)} of {Hq * nb} rows")
+    # --- BSA: sampled (head, row) pairs with the GPU's lists, spread over rows,
+    # one oracle call (it allocates full-size outputs once per call)
+    idx_c, cnt_c = idx.cpu().numpy(), cnt.cpu().numpy()
+    hs = [0, G, 2 * G, 3 * G]
+    sample_rows = [int(x) for x in np.linspace(nb - 1, 0, 24)]
+    qs = q[:, hs, :].to(torch.float64).numpy()
+    ks = k[:, 0:4, :].to(torch.float64).numpy()
+    vs = v[:, 0:4, :].to(torch.float64).numpy()
+    li, lc = idx_c[hs], cnt_c[hs]
+    work = [(j, r) for r in sample_rows for j in range(len(hs))]
+    t0 = time.perf_counter()
+    O.block_sparse_attention(qs, ks, vs, li, lc, [0, L], len(hs), 4, sc, rows=work)
+    t_bs = time.perf_counter() - t0
+    done = sum((int(lc[j, r]) - 1) * 16384 + 8256 for j, r in work)
+    est_bsa = t_bs * bsa_pairs_total[0] / done
+    parts.append(f"bsa: {len(work)} (head, query-block) rows, {done} of {bsa_pairs_total[0]} token pairs")
+    est_total = est_score + est_topk + est_bsa
+    return {"value": gpu_flop_dense / est_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "; ".join(parts) + f"; measured {t_vn + t_sc + t_tk + t_bs:.1f} s, scaled by work "
+                      f"to an estimated {est_total:.0f} s per layer (extrapolated)",
+            "est_stage_s": {"score": est_score, "schedule": est_topk, "bsa": est_bsa}}
+
+
+bsa_pairs_total = [0]
+
+
+def run_main(args):
+    import torch
+    import block_sparse_attention_stem_amd as stem
+    import stem_synth as S
+
+    dev = torch.device("cuda:0")
+    w = S.CONFIGS[args.workload]
+    p = stem.Problem(w.cu_seqlens, w.num_q_heads, w.num_kv_heads)
+    log(f"[bench] generating {w.name}: T={w.total_tokens} Hq={w.num_q_heads} Hkv={w.num_kv_heads}")
+    q, k, v = S.make_workload_qkv(w)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    scores = torch.empty((p.Hq, p.R, p.max_nb), dtype=torch.float32, device=dev)
+    ws = torch.empty(stem.stem_score_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    kcap = stem.stem_max_kept(p, w.k_start, w.mu, w.alpha, w.n_init, w.n_window)
+    idx = torch.empty((p.Hq, p.R, kcap), dtype=torch.int32, device=dev)
+    cnt = torch.empty((p.Hq, p.R), dtype=torch.int32, device=dev)
+    out = torch.empty((p.T, p.Hq, 128), dtype=torch.bfloat16, device=dev)
+    dout = torch.empty_like(out)
+
+    fns = [lambda: stem.stem_score(p, qd, kd, vd, w.stride, w.chunk_size, w.norm, w.beta, scores, ws),
+           lambda: stem.stem_schedule_topk(p, scores, w.k_start, w.mu, w.alpha, w.n_init, w.n_window,
+                                           kcap, idx, cnt),
+           lambda: stem.stem_bsa_prefill(p, qd, kd, vd, idx, cnt, out=out)]
+    timer = StageTimer(torch, ["score", "schedule", "bsa"])
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        timer.run(fns)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    evs = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        evs.append(timer.run(fns))
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    for ev in evs:
+        timer.collect(ev)
+
+    dtimer = StageTimer(torch, ["dense"])
+    dfn = [lambda: stem.stem_dense_prefill(p, qd, kd, vd, out=dout)]
+    for _ in range(max(1, args.warmup)):
+        dtimer.run(dfn)
+    torch.cuda.synchronize()
+    devs = [dtimer.run(dfn) for _ in range(max(3, args.steps // 2))]
+    torch.cuda.synchronize()
+    for ev in devs:
+        dtimer.collect(ev)
+
+    flop_dense = dense_flop(w.seqlens, w.num_q_heads)
+    pairs = bsa_pairs(idx, cnt, p)
+    bsa_pairs_total[0] = pairs
+    dense_pairs = w.num_q_heads * sum(L * (L + 1) / 2 for L in w.seqlens)
+    rho = pairs / dense_pairs
+    kept_blocks = int(cnt.sum().item())
+    causal_blocks = w.num_q_heads * sum(nb * (nb + 1) // 2 for nb in p.nbs)
+    t_stem = timer.mean("score") + timer.mean("schedule") + timer.mean("bsa")
+    t_dense = dtimer.mean("dense")
+    bsa_flop = 4.0 * 128 * pairs
+    score_flop = 2.0 * 16 * 16 * 1024 * causal_blocks
+    bsa_tflops = bsa_flop / (timer.mean("bsa") * 1e-3) / 1e12
+    topk_bytes = 4.0 * causal_blocks + 4.0 * (idx.numel() + cnt.numel())
+    traffic = load_traffic("attn_bf16_sparse_cfg3", source_sha("attn.hip", "gfx950_util.h"))
+
+    res = {
+        "metric": METRIC,
+        "value": flop_dense / (t_stem * 1e-3) / 1e12,
+        "unit": "TFLOP/s (effective: dense-equivalent causal FLOP / Stem score+schedule+BSA time)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": t_stem,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "cfg3: one attention layer, batch 1, N=131072, 32 q heads / 8 kv heads, "
+                               "head_dim 128, bf16 N(0,1) Q/K/V with +3 sigma sink keys and lognormal V "
+                               "rows; block 128, stride 8, chunk 2048, beta 0.2, k_start 276, alpha 0.7, "
+                               "mu 0.5, 1 sink + 2 window blocks",
+                   "seq_len": w.total_tokens, "kept_block_fraction": kept_blocks / causal_blocks,
+                   "computed_pair_fraction": rho},
+        "stages_ms": {"score": timer.mean("score"), "schedule": timer.mean("schedule"),
+                      "bsa": timer.mean("bsa"), "wall_per_step": wall_ms},
+        "dense_ms": t_dense,
+        "dense_tflops": flop_dense / (t_dense * 1e-3) / 1e12,
+        "speedup_vs_dense": t_dense / t_stem,
+        "bsa_speedup_vs_dense": t_dense / timer.mean("bsa"),
+        "skip_overhead": timer.mean("bsa") / (rho * t_dense) - 1.0,
+        "score_mfma_tflops": score_flop / (timer.mean("score") * 1e-3) / 1e12,
+        "schedule_gbs": topk_bytes / (timer.mean("schedule") * 1e-3) / 1e9,
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<sparse>",
+                     "achieved": bsa_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": bsa_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": traffic,
+                     "algorithmic_flop_per_launch": bsa_flop},
+    }
+    log(f"[bench] stem {t_stem:.2f} ms (score {timer.mean('score'):.2f}, schedule "
+        f"{timer.mean('schedule'):.3f}, bsa {timer.mean('bsa'):.2f}); dense {t_dense:.2f} ms")
+
+    if not args.no_sweep:
+        res["density_sweep"] = density_sweep(args, torch, stem, S, dev)
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle, bounded sample)")
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, idx, cnt, flop_dense)
+    print(json.dumps(res), flush=True)
+
+
+def density_sweep(args, torch, stem, S, dev):
+    """Config 4: N = 65536, keep 100/50/25/20/10 %: BSA time vs computed fraction."""
+    w0 = S.sweep_workload(1.0)
+    p = stem.Problem(w0.cu_seqlens, w0.num_q_heads, w0.num_kv_heads)
+    log("[bench] density sweep: generating N=65536 inputs")
+    q, k, v = S.make_workload_qkv(w0)
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    del q, k, v
+    out = torch.empty((p.T, p.Hq, 128), dtype=torch.bfloat16, device=dev)
+    scores = stem.stem_score(p, qd, kd, vd)
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        evs = []
+        for _ in range(n):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        return ts[len(ts) // 2]
+
+    t_dense = timed(lambda: stem.stem_dense_prefill(p, qd, kd, vd, out=out), 5)
+    dense_pairs = p.Hq * sum(L * (L + 1) / 2 for L in w0.seqlens)
+    pts = []
+    for keep in sorted(S.SWEEP_N64K, reverse=True):
+        w = S.sweep_workload(keep)
+        idx, cnt = stem.stem_schedule_topk(p, scores, w.k_start, w.mu, w.alpha, w.n_init, w.n_window)
+        t = timed(lambda: stem.stem_bsa_prefill(p, qd, kd, vd, idx, cnt, out=out), 5)
+        rho = bsa_pairs(idx, cnt, p) / dense_pairs
+        pts.append({"target_keep": keep, "k_start": w.k_start[0], "computed_pair_fraction": rho,
+                    "bsa_ms": t, "skip_overhead": t / (rho * t_dense) - 1.0})
+        log(f"[bench]   keep {keep:.2f}: rho {rho:.4f} bsa {t:.2f} ms")
+    xs = [pt["computed_pair_fraction"] for pt in pts]
+    ys = [pt["bsa_ms"] for pt in pts]
+    n = len(xs)
+    mx, my = sum(xs) / n, sum(ys) / n
+    sxx = sum((x - mx) ** 2 for x in xs)
+    sxy = sum((x - mx) * (y - my) for x, y in zip(xs, ys))
+    b = sxy / sxx
+    a = my - b * mx
+    ss_res = sum((y - (a + b * x)) ** 2 for x, y in zip(xs, ys))
+    ss_tot = sum((y - my) ** 2 for y in ys)
+    return {"workload": "cfg4: N=65536, 32q/8kv, d128, alpha 0.7, mu 0.5, 1 sink + 2 window",
+            "dense_ms": t_dense, "points": pts,
+            "linear_fit_ms": {"intercept": a, "slope": b, "r2": 1 - ss_res / ss_tot}}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="cfg3_n128k")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the Stem path here runs on a single MI355X "
+              "(no sharding or collectives); run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    run_main(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,119 @@
+// Internal declarations shared by the gfx950 kernels and the C-ABI layer.
+// Nothing here is part of the public ABI (include/stem.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <math.h>
+
+namespace stem {
+
+constexpr int kBlock = 128;           // attention block (tokens)
+constexpr int kHeadDim = 128;         // head dimension
+constexpr int kMaxSeqsPerLaunch = 64; // sequences described inline per launch
+constexpr int kMaxRowBlocks = 2048;   // top-k row length limit (256K tokens)
+
+// Packed-batch description passed BY VALUE to every kernel (no device
+// metadata buffers).  Offsets are global: tok[z] is the first packed token of
+// sequence z of this launch, row[z] its first global block row (tok[z]/128).
+// item[z] is a per-kernel prefix of work items (set by the launcher).
+struct SeqTable {
+  int32_t n;
+  int32_t tok[kMaxSeqsPerLaunch + 1];
+  int32_t row[kMaxSeqsPerLaunch + 1];
+  int32_t item[kMaxSeqsPerLaunch + 1];
+};
+
+// Locate the sequence of this launch that contains `x`, where `off` is a
+// non-decreasing prefix array of n+1 entries (row offsets or item offsets).
+__device__ __forceinline__ int seq_of(const int32_t *off, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {               // largest z with off[z] <= x
+    int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Work-item order for a grid whose hardware dispatch sends workgroup b to
+// XCD b % 8 (MI355X: 8 XCDs, each with its own L2).  Items are "slots"
+// (a row or tile of one KV group) times G query heads.  In every round of
+// 8*G consecutive workgroups, the 8 XCDs take 8 consecutive slots and each
+// XCD runs all G heads of its slot, so the heads that share K/V meet in one
+// L2 and the whole chip walks the same KV head at the same time.
+// Returns slot * G + head.
+__device__ __forceinline__ int xcd_item(int b, int n_items, int G) {
+  const int per_round = 8 * G;
+  const int full = (n_items / per_round) * per_round;
+  if (b >= full) return b;                       // ragged last round: identity
+  const int round = b / per_round, j = b - round * per_round;
+  const int slot = round * 8 + (j & 7);
+  return slot * G + (j >> 3);
+}
+
+// Token-Position-Decay budget: k(I) = floor(ke - ke (1 - mu) I / nb), with
+// ke = alpha * k_start already folded in.  Evaluated in fp64 without
+// contraction; the 1e-9 nudge absorbs the rounding of the fp64 steps when the
+// exact (decimal) value is an integer.
+__host__ __device__ inline int tpd_budget(int I, int nb, double ke, double mu) {
+#pragma clang fp contract(off)
+  const double slope = ke * (1.0 - mu);
+  const double dec = slope * (double)I / (double)nb;
+  const double x = ke - dec;
+  return (int)floor(x + 1e-9);
+}
+
+__host__ __device__ inline int forced_count(int I, int n_init, int n_window) {
+  // |[0, min(n_init, I+1)) U [max(0, I-n_window+1), I]|
+  const int a = n_init < I + 1 ? n_init : I + 1;          // sinks [0, a)
+  int w0 = I - n_window + 1; if (w0 < 0) w0 = 0;         // window [w0, I]
+  const int wn = n_window > 0 ? I - w0 + 1 : 0;
+  if (wn == 0) return a;
+  const int overlap = a > w0 ? a - w0 : 0;
+  return a + wn - overlap;
+}
+
+__host__ __device__ inline int kept_count(int I, int nb, double ke, double mu,
+                                          int n_init, int n_window) {
+  int k = tpd_budget(I, nb, ke, mu);
+  const int f = forced_count(I, n_init, n_window);
+  if (k < f) k = f;
+  return k < I + 1 ? k : I + 1;
+}
+
+// ---------------------------------------------------------------- launchers
+struct ScoreLaunch {
+  const void *q, *k, *v;
+  float *scores, *ell;          // ell: workspace [Hkv][R] (log norms, then bonus)
+  int32_t Hq, Hkv, R, max_nb;
+  int32_t stride, chunk_size;
+  float scale, beta;
+};
+hipError_t launch_vnorm(const ScoreLaunch &a, hipStream_t s);
+hipError_t launch_vstats(const ScoreLaunch &a, const SeqTable &t, hipStream_t s);
+hipError_t launch_score(const ScoreLaunch &a, const SeqTable &t, int n_items, hipStream_t s);
+
+struct TopkLaunch {
+  const float *scores;
+  int32_t *idx, *cnt;
+  int32_t Hq, R, max_nb, k_cap;
+  double mu;
+  int32_t n_init, n_window;
+  double ke[kMaxSeqsPerLaunch];
+};
+hipError_t launch_topk(const TopkLaunch &a, const SeqTable &t, int rows_in_launch, hipStream_t s);
+
+struct AttnLaunch {
+  const void *q, *k, *v;
+  const float *q_scale, *k_scale, *v_scale;
+  const int32_t *idx, *cnt;
+  int32_t k_cap;
+  void *out;
+  float *lse;
+  int32_t Hq, Hkv, R, T;
+  float scale_log2;              // softmax_scale * log2(e)
+};
+hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows_in_launch,
+                       bool sparse, bool fp8, hipStream_t s);
+
+}  // namespace stem

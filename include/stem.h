@@ -1,0 +1,175 @@
+/*
+ * stem.h - C ABI of the MI355X (gfx950) Stem sparse-prefill attention library.
+ *
+ * The path has three stages, each one entry point:
+ *   stem_score          block-level scoring: stride-s anti-diagonal down-sampled
+ *                       Q.K^T, max-pooled to block x block scores, plus the
+ *                       output-aware value bonus.
+ *   stem_schedule_topk  Token-Position-Decay budget per query block, sink and
+ *                       window blocks forced, per-row top-k -> compact lists.
+ *   stem_bsa_prefill    causal block-sparse flash attention over those lists
+ *                       (bf16, or fp8 e4m3 with per-block scales).
+ * plus stem_dense_prefill, the library's own dense causal attention (the
+ * baseline every speed-up is measured against).
+ *
+ * Sources: AngelSlim documentation "Stem: Rethinking Causal Information Flow in
+ * Sparse Attention" (features/sparse_attention/stem.md) §2.1-2.3 and the §6
+ * parameter table; gist.science summary of the Stem paper, §2.1 (TPD budget)
+ * and §2.2 (OAM metric).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensor pointers are DEVICE memory owned by the caller; the library keeps
+ *    no pointer after the call returns and allocates nothing.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *    default stream).  The host never waits for the device.
+ *  - Arguments are validated before anything is enqueued; an invalid call
+ *    returns a non-zero stem_status_t and enqueues nothing.  A launch failure
+ *    returns STEM_ERR_HIP.  Device-side faults surface at the caller's next
+ *    synchronisation on that stream.
+ *  - Calls on different streams are independent; the library holds no state
+ *    and is thread-safe.
+ *  - Token-major layouts: Q is [T][Hq][d], K and V are [T][Hkv][d] (row
+ *    stride H*d elements), T = total packed tokens.  Sequences are packed back
+ *    to back; cu_seqlens holds the num_seqs+1 token offsets.  Query head h
+ *    reads KV head h / (Hq / Hkv) (grouped-query attention).
+ *  - Blocks are counted per sequence: sequence z has nb_z = L_z / block_size
+ *    blocks, and query-block rows are numbered globally r = 0 .. R-1 with
+ *    R = sum_z nb_z (key blocks use the same global numbering).  max_nb =
+ *    max_z nb_z.
+ */
+#ifndef STEM_H_
+#define STEM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  STEM_OK = 0,
+  STEM_ERR_INVALID_ARG = 1,   /* null pointer, bad size, inconsistent shape  */
+  STEM_ERR_UNSUPPORTED = 2,   /* valid but not implemented (head_dim != 128,
+                                 block_size != 128, ragged tail block, ...)  */
+  STEM_ERR_CAPACITY = 3,      /* k_cap smaller than a row's kept count       */
+  STEM_ERR_WORKSPACE = 4,     /* workspace missing or too small              */
+  STEM_ERR_HIP = 5            /* a HIP launch or runtime call failed         */
+} stem_status_t;
+
+typedef enum {
+  STEM_DTYPE_BF16 = 0,        /* bfloat16 Q/K/V                              */
+  STEM_DTYPE_FP8_E4M3 = 1     /* OCP e4m3fn codes with fp32 per-block scales  */
+} stem_dtype_t;
+
+/* One packed batch of sequences (the shape of the problem). */
+typedef struct {
+  int32_t num_seqs;                 /* B >= 1                                   */
+  const int32_t *cu_seqlens_host;   /* HOST [B+1]: 0 = c0 < c1 < ..., every
+                                       length c[z+1]-c[z] a positive multiple of
+                                       block_size.  Read during the call only;
+                                       the kernels receive the offsets by value */
+  int32_t num_q_heads;              /* Hq, a multiple of num_kv_heads           */
+  int32_t num_kv_heads;             /* Hkv >= 1                                 */
+  int32_t head_dim;                 /* d; 128 is the supported value            */
+  int32_t block_size;               /* attention block; 128 is supported        */
+} stem_problem_t;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *stem_status_string(int status);
+
+/* ---------------------------------------------------------------------------
+ * Stage 1: block scores.  AngelSlim Stem doc §2.1: score(Q_i, K_j) =
+ * Q_i.K_j^T / (sqrt(d) s n) + lambda ReLU(vbar_j), computed by a strided
+ * group GEMM with stride s and chunk width chunk_size; gist.science summary
+ * §2.2-2.3: anti-diagonal down-sampling of Q and K, block-wise max pooling,
+ * value magnitude from block max pooling.
+ *
+ * For sequence z, query head h, KV head g, strided rows i, j in [0, L_z/s):
+ *   A[i][j] = sum_{t<s} Q[c_z + i s + t][h] . K[c_z + j s + s-1-t][g]
+ *             / (sqrt(d) * s * norm),     defined for j <= i
+ *   S[h][r(z,I)][J] = max over the (block/s)^2 strided cells of block pair
+ *                     (I, J) with j <= i, plus bonus[g][J], for J <= I
+ *   bonus[g][J] = beta * max(0, (l_J - mean_z(l)) / (std_z(l) + 1e-6)),
+ *   l_J = ln max_{t in key block J} ||V[t][g]||^2, mean and population std
+ *   taken over the nb_z key blocks of sequence z.
+ * S is fp32 [Hq][R][max_nb]; every entry with J > I or J >= nb_z is -inf.
+ * q, k, v: bf16.  stride divides block_size; chunk_size is a positive
+ * multiple of block_size (it orders the work, it changes no value).
+ * workspace: device memory of at least stem_score_workspace_bytes(p) bytes,
+ * 256-byte aligned; its contents on return are unspecified.
+ * ------------------------------------------------------------------------- */
+size_t stem_score_workspace_bytes(const stem_problem_t *p);
+int stem_score(const stem_problem_t *p, const void *q, const void *k, const void *v,
+               int32_t stride, int32_t chunk_size, float norm, float beta,
+               float *scores, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Stage 2: schedule + top-k.  gist.science summary §2.1 (TPD): per query
+ * block I of a sequence with nb blocks, k(I) = floor(ke - ke (1-mu) I / nb),
+ * ke = alpha * k_start (alpha: this layer's factor, AngelSlim doc §2.2);
+ * AngelSlim doc §2.2 / zhichai summary §三: the first n_init blocks (sinks)
+ * and the n_window blocks ending at I are always kept.
+ *   F(I)     = [0, min(n_init, I+1)) U [max(0, I-n_window+1), I]
+ *   kept(I)  = min(I+1, max(k(I), |F(I)|))
+ * Row (h, r) lists F(I) plus the kept(I)-|F(I)| best other blocks J <= I by
+ * score (descending; equal scores -> lower J first; NaN ranks as -inf),
+ * in ascending order.  block_idx: int32 [Hq][R][k_cap], entries past the
+ * count are -1; block_cnt: int32 [Hq][R].
+ * k_start_host: HOST [B] budgets in blocks (before alpha), >= 0.
+ * mu in (0, 1], alpha > 0, n_init >= 0, n_window >= 0.
+ * k(I) is evaluated in fp64 as floor(x + 1e-9): exact whenever the
+ * parameters' decimal values have denominators far below 1e9 (e.g. 0.7 =
+ * 7/10), which every documented setting has.
+ * Returns STEM_ERR_CAPACITY if k_cap < stem_max_kept(...).  Requires
+ * max_nb <= 2048 (sequences up to 256K tokens at block 128).
+ * ------------------------------------------------------------------------- */
+int stem_schedule_topk(const stem_problem_t *p, const float *scores,
+                       const double *k_start_host, double mu, double alpha,
+                       int32_t n_init, int32_t n_window, int32_t k_cap,
+                       int32_t *block_idx, int32_t *block_cnt, void *stream);
+
+/* Host-only helpers (no device work): the budget rule above, and the
+ * largest kept(I) over every row of the problem (a safe k_cap). */
+int32_t stem_tpd_budget(int32_t I, int32_t nb, double k_start, double mu, double alpha);
+int32_t stem_kept_count(int32_t I, int32_t nb, double k_start, double mu, double alpha,
+                        int32_t n_init, int32_t n_window);
+int32_t stem_max_kept(const stem_problem_t *p, const double *k_start_host, double mu,
+                      double alpha, int32_t n_init, int32_t n_window);
+
+/* ---------------------------------------------------------------------------
+ * Stage 3: causal block-sparse attention.  AngelSlim doc §2.3: exact
+ * attention on the selected blocks only; youleyou HPC-BSA article §三.3.1: a
+ * skipped block is equivalent to all its scores being -inf.
+ * For row (h, r) = (h, block I of sequence z), queries t in block I attend to
+ * the keys of the listed blocks J (local to z) with key position <= query
+ * position: out[t][h] = sum_u softmax_u(softmax_scale * q_t.k_u) v_u.
+ * A row with count 0 gives out = 0 and lse = -inf.
+ * dtype BF16: q, k, v bf16; scales must be NULL.
+ * dtype FP8_E4M3: q, k, v are e4m3fn codes (uint8); the real value of an
+ *   element of token block b (global) and head x is code * scale[b][x]:
+ *   q_scale fp32 [R][Hq], k_scale and v_scale fp32 [R][Hkv].
+ * block_idx / block_cnt as produced by stem_schedule_topk (k_cap = its row
+ *   stride; entries must be ascending, in [0, I]).
+ * out: bf16 [T][Hq][d].  lse: optional fp32 [Hq][T] (natural log), may be NULL.
+ * ------------------------------------------------------------------------- */
+int stem_bsa_prefill(const stem_problem_t *p, int32_t dtype, const void *q, const void *k,
+                     const void *v, const float *q_scale, const float *k_scale,
+                     const float *v_scale, const int32_t *block_idx,
+                     const int32_t *block_cnt, int32_t k_cap, float softmax_scale,
+                     void *out, float *lse, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Dense causal attention with the same tile kernel (every causal block).
+ * Same arguments and outputs as stem_bsa_prefill without the lists.
+ * ------------------------------------------------------------------------- */
+int stem_dense_prefill(const stem_problem_t *p, int32_t dtype, const void *q, const void *k,
+                       const void *v, const float *q_scale, const float *k_scale,
+                       const float *v_scale, float softmax_scale, void *out, float *lse,
+                       void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STEM_H_ */

@@ -1,0 +1,142 @@
+"""CPU-only checks of the C ABI: the library loads, exports every symbol that
+include/stem.h declares, its host-side budget rule equals the oracle's exact
+rational TPD on every row of every workload, and invalid calls are rejected
+before anything touches a device (no compute calls here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_stem_amd as stem
+import oracle as O
+import stem_synth as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    src = open(os.path.join(ROOT, "include", "stem.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(stem_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = stem.load_library()
+    names = _declared_symbols()
+    assert len(names) >= 9
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(stem.EXPORTED)
+
+
+def test_status_strings():
+    lib = stem.load_library()
+    for code, name in stem.STATUS.items():
+        assert lib.stem_status_string(code).decode() == name
+    assert lib.stem_status_string(99).decode() == "STEM_ERR_UNKNOWN"
+
+
+def _all_workloads():
+    ws = list(S.CONFIGS.values()) + [S.sweep_workload(k) for k in S.SWEEP_N64K] + \
+        [S.fp8_workload(0), S.fp8_workload(5)]
+    return ws
+
+
+@pytest.mark.parametrize("w", _all_workloads(), ids=lambda w: w.name)
+def test_host_budget_matches_oracle_exact_rationals_on_every_row(w):
+    for z, L in enumerate(w.seqlens):
+        nb = L // 128
+        for I in range(nb):
+            assert stem.stem_tpd_budget(I, nb, w.k_start[z], w.mu, w.alpha) == \
+                O.tpd_budget(I, nb, w.k_start[z], w.mu, w.alpha)
+            assert stem.stem_kept_count(I, nb, w.k_start[z], w.mu, w.alpha, w.n_init, w.n_window) == \
+                O.kept_count(I, nb, w.k_start[z], w.mu, w.alpha, w.n_init, w.n_window)
+
+
+@pytest.mark.parametrize("params", [(13, 0.7, 1.0, 1, 1), (100, 0.3, 0.7, 4, 4), (5, 1.0, 0.7, 0, 0),
+                                    (37, 0.55, 0.9, 2, 3), (0, 0.5, 1.0, 2, 0)])
+def test_host_budget_matches_oracle_other_parameters(params):
+    ks, mu, alpha, ni, nw = params
+    for nb in (1, 7, 64, 333):
+        for I in range(nb):
+            assert stem.stem_kept_count(I, nb, ks, mu, alpha, ni, nw) == \
+                O.kept_count(I, nb, ks, mu, alpha, ni, nw)
+
+
+def test_max_kept_is_the_row_maximum():
+    w = S.fp8_workload(6)
+    p = stem.Problem(w.cu_seqlens, 32, 8)
+    got = stem.stem_max_kept(p, w.k_start, w.mu, w.alpha, w.n_init, w.n_window)
+    ref = max(O.kept_count(I, L // 128, w.k_start[z], w.mu, w.alpha, w.n_init, w.n_window)
+              for z, L in enumerate(w.seqlens) for I in range(L // 128))
+    assert got == ref
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation
+
+
+def _score(p, stride=8, chunk=2048, norm=1.0, beta=0.2, ws=FAKE, wsb=1 << 20, q=FAKE):
+    return stem.load_library().stem_score(p.ref, q, FAKE, FAKE, stride, chunk, norm, beta, FAKE,
+                                          ws, wsb, None)
+
+
+def test_score_argument_errors():
+    p = stem.Problem([0, 1024], 4, 2)
+    assert _score(p, q=None) == 1
+    assert _score(p, stride=3) == 1
+    assert _score(p, stride=4) == 2                      # valid, not implemented
+    assert _score(p, chunk=100) == 1
+    assert _score(p, norm=0.0) == 1
+    assert _score(p, beta=-1.0) == 1
+    assert _score(p, ws=None) == 4
+    assert _score(p, wsb=8) == 4
+    assert _score(p, ws=ctypes.c_void_p(0x1004)) == 4    # misaligned
+    assert _score(stem.Problem([0, 1000], 4, 2)) == 2    # ragged tail block
+    assert _score(stem.Problem([0, 1024], 4, 3)) == 1    # Hq % Hkv != 0
+    assert _score(stem.Problem([0, 1024], 4, 2, head_dim=64)) == 2
+    assert _score(stem.Problem([0, 1024], 4, 2, block_size=64)) == 2
+    assert _score(stem.Problem([0, 1024, 1024], 4, 2)) == 1   # empty sequence
+    assert stem.stem_score_workspace_bytes(stem.Problem([0, 1024], 4, 2)) == 256
+
+
+def test_schedule_argument_errors():
+    lib = stem.load_library()
+    p = stem.Problem([0, 4096], 4, 2)
+    ks = (ctypes.c_double * 1)(10.0)
+
+    def call(mu=0.5, alpha=1.0, ni=1, nw=1, cap=32, kss=ks, idx=FAKE):
+        return lib.stem_schedule_topk(p.ref, FAKE, kss, mu, alpha, ni, nw, cap, idx, FAKE, None)
+    assert call(mu=0.0) == 1
+    assert call(mu=1.5) == 1
+    assert call(alpha=0.0) == 1
+    assert call(ni=-1) == 1
+    assert call(idx=None) == 1
+    assert call(kss=(ctypes.c_double * 1)(-1.0)) == 1
+    assert stem.stem_max_kept(p, 10.0, 0.5, 1.0, 1, 1) == 8   # rows 7..9 keep 8 blocks
+    assert call(cap=7) == 3
+    big = stem.Problem([0, 128 * 4096], 4, 2)
+    assert lib.stem_schedule_topk(big.ref, FAKE, ks, 0.5, 1.0, 1, 1, 4096, FAKE, FAKE, None) == 2
+
+
+def test_attention_argument_errors():
+    lib = stem.load_library()
+    p = stem.Problem([0, 1024], 4, 2)
+    f = FAKE
+    assert lib.stem_bsa_prefill(p.ref, 0, f, f, f, None, None, None, None, f, 8, 0.1, f, None, None) == 1
+    assert lib.stem_bsa_prefill(p.ref, 0, f, f, f, f, None, None, f, f, 8, 0.1, f, None, None) == 1
+    assert lib.stem_bsa_prefill(p.ref, 1, f, f, f, None, None, None, f, f, 8, 0.1, f, None, None) == 1
+    assert lib.stem_bsa_prefill(p.ref, 7, f, f, f, None, None, None, f, f, 8, 0.1, f, None, None) == 2
+    assert lib.stem_bsa_prefill(p.ref, 0, f, f, f, None, None, None, f, f, 0, 0.1, f, None, None) == 1
+    assert lib.stem_dense_prefill(p.ref, 0, f, f, f, None, None, None, -1.0, f, None, None) == 1
+    assert lib.stem_dense_prefill(p.ref, 0, None, f, f, None, None, None, 0.1, f, None, None) == 1
+
+
+def test_package_defaults_match_the_doc_table():
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "stem_doc_defaults.json")))
+    for k, v in g["defaults"].items():
+        assert stem.DEFAULTS[k] == v, k
+    assert stem.DEFAULTS["beta"] == g["beta"]["value"]
+    a = g["alpha_list_example"]
+    assert list(S.FP8_ALPHAS) == [a["warmup_alpha"]] * a["warmup_layers"] + [a["later_alpha"]] * a["later_layers"]
