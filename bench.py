@@ -197,11 +197,12 @@ def run_main(args):
     cnt = torch.empty((p.Hq, p.R), dtype=torch.int32, device=dev)
     out = torch.empty((p.T, p.Hq, 128), dtype=torch.bfloat16, device=dev)
     dout = torch.empty_like(out)
+    aws = torch.empty(stem.stem_attn_workspace_bytes(p, stem.STEM_DTYPE_BF16), dtype=torch.uint8, device=dev)
 
     fns = [lambda: stem.stem_score(p, qd, kd, vd, w.stride, w.chunk_size, w.norm, w.beta, scores, ws),
            lambda: stem.stem_schedule_topk(p, scores, w.k_start, w.mu, w.alpha, w.n_init, w.n_window,
                                            kcap, idx, cnt),
-           lambda: stem.stem_bsa_prefill(p, qd, kd, vd, idx, cnt, out=out)]
+           lambda: stem.stem_bsa_prefill(p, qd, kd, vd, idx, cnt, out=out, workspace=aws)]
     timer = StageTimer(torch, ["score", "schedule", "bsa"])
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -218,7 +219,7 @@ def run_main(args):
         timer.collect(ev)
 
     dtimer = StageTimer(torch, ["dense"])
-    dfn = [lambda: stem.stem_dense_prefill(p, qd, kd, vd, out=dout)]
+    dfn = [lambda: stem.stem_dense_prefill(p, qd, kd, vd, out=dout, workspace=aws)]
     for _ in range(max(1, args.warmup)):
         dtimer.run(dfn)
     torch.cuda.synchronize()
@@ -291,6 +292,7 @@ def density_sweep(args, torch, stem, S, dev):
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     del q, k, v
     out = torch.empty((p.T, p.Hq, 128), dtype=torch.bfloat16, device=dev)
+    aws = torch.empty(stem.stem_attn_workspace_bytes(p, stem.STEM_DTYPE_BF16), dtype=torch.uint8, device=dev)
     scores = stem.stem_score(p, qd, kd, vd)
 
     def timed(fn, n):
@@ -307,13 +309,13 @@ def density_sweep(args, torch, stem, S, dev):
         ts = sorted(a.elapsed_time(b) for a, b in evs)
         return ts[len(ts) // 2]
 
-    t_dense = timed(lambda: stem.stem_dense_prefill(p, qd, kd, vd, out=out), 5)
+    t_dense = timed(lambda: stem.stem_dense_prefill(p, qd, kd, vd, out=out, workspace=aws), 5)
     dense_pairs = p.Hq * sum(L * (L + 1) / 2 for L in w0.seqlens)
     pts = []
     for keep in sorted(S.SWEEP_N64K, reverse=True):
         w = S.sweep_workload(keep)
         idx, cnt = stem.stem_schedule_topk(p, scores, w.k_start, w.mu, w.alpha, w.n_init, w.n_window)
-        t = timed(lambda: stem.stem_bsa_prefill(p, qd, kd, vd, idx, cnt, out=out), 5)
+        t = timed(lambda: stem.stem_bsa_prefill(p, qd, kd, vd, idx, cnt, out=out, workspace=aws), 5)
         rho = bsa_pairs(idx, cnt, p) / dense_pairs
         pts.append({"target_keep": keep, "k_start": w.k_start[0], "computed_pair_fraction": rho,
                     "bsa_ms": t, "skip_overhead": t / (rho * t_dense) - 1.0})

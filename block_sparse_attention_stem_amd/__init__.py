@@ -37,7 +37,7 @@ DEFAULTS = dict(block_size=128, stride=8, chunk_size=2048, norm=1.0,
 
 EXPORTED = ("stem_status_string", "stem_score_workspace_bytes", "stem_score",
             "stem_schedule_topk", "stem_tpd_budget", "stem_kept_count", "stem_max_kept",
-            "stem_bsa_prefill", "stem_dense_prefill")
+            "stem_attn_workspace_bytes", "stem_bsa_prefill", "stem_dense_prefill")
 
 
 class StemError(RuntimeError):
@@ -82,9 +82,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.stem_kept_count.restype = i32
     lib.stem_max_kept.argtypes = [P, ctypes.POINTER(f64), f64, f64, i32, i32]
     lib.stem_max_kept.restype = i32
-    lib.stem_bsa_prefill.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp]
+    lib.stem_attn_workspace_bytes.argtypes = [P, i32]
+    lib.stem_attn_workspace_bytes.restype = sz
+    lib.stem_bsa_prefill.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
     lib.stem_bsa_prefill.restype = ctypes.c_int
-    lib.stem_dense_prefill.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp]
+    lib.stem_dense_prefill.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
     lib.stem_dense_prefill.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -217,9 +219,22 @@ def _attn_inputs(p: Problem, q, k, v, scales):
     return dt, (qs, kss, vs)
 
 
+def stem_attn_workspace_bytes(p: Problem, dtype: int = STEM_DTYPE_BF16) -> int:
+    return int(load_library().stem_attn_workspace_bytes(p.ref, dtype))
+
+
+def _attn_workspace(p: Problem, dt: int, workspace, device):
+    n = stem_attn_workspace_bytes(p, dt)
+    if workspace is None:
+        workspace = torch.empty(n, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < n:
+        raise ValueError(f"workspace: need {n} bytes")
+    return workspace
+
+
 def stem_bsa_prefill(p: Problem, q, k, v, block_idx, block_cnt, softmax_scale: Optional[float] = None,
                      scales=None, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                     want_lse: bool = False, stream=None):
+                     want_lse: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
     """Causal block-sparse attention over the lists: out bf16 [T][Hq][d] (+ lse fp32 [Hq][T])."""
     lib = load_library()
     dt, (qs, kss, vs) = _attn_inputs(p, q, k, v, scales)
@@ -235,16 +250,18 @@ def stem_bsa_prefill(p: Problem, q, k, v, block_idx, block_cnt, softmax_scale: O
         lse = torch.empty((p.Hq, p.T), dtype=torch.float32, device=q.device)
     if lse is not None:
         _need(lse, "lse", torch.float32, (p.Hq, p.T))
+    ws = _attn_workspace(p, dt, workspace, q.device)
     st = lib.stem_bsa_prefill(p.ref, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(qs), _ptr(kss), _ptr(vs),
                               _ptr(block_idx), _ptr(block_cnt), int(block_idx.shape[2]), scale,
-                              _ptr(out), _ptr(lse), _stream(stream))
+                              _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                              _stream(stream))
     _check("stem_bsa_prefill", st)
     return (out, lse) if lse is not None else out
 
 
 def stem_dense_prefill(p: Problem, q, k, v, softmax_scale: Optional[float] = None, scales=None,
                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                       want_lse: bool = False, stream=None):
+                       want_lse: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
     """Dense causal attention with the same tile kernel."""
     lib = load_library()
     dt, (qs, kss, vs) = _attn_inputs(p, q, k, v, scales)
@@ -256,8 +273,10 @@ def stem_dense_prefill(p: Problem, q, k, v, softmax_scale: Optional[float] = Non
         lse = torch.empty((p.Hq, p.T), dtype=torch.float32, device=q.device)
     if lse is not None:
         _need(lse, "lse", torch.float32, (p.Hq, p.T))
+    ws = _attn_workspace(p, dt, workspace, q.device)
     st = lib.stem_dense_prefill(p.ref, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(qs), _ptr(kss), _ptr(vs),
-                                scale, _ptr(out), _ptr(lse), _stream(stream))
+                                scale, _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(stream))
     _check("stem_dense_prefill", st)
     return (out, lse) if lse is not None else out
 

@@ -202,11 +202,18 @@ int stem_schedule_topk(const stem_problem_t *p, const float *scores, const doubl
   return STEM_OK;
 }
 
+size_t stem_attn_workspace_bytes(const stem_problem_t *p, int32_t dtype) {
+  Shape s;
+  if (check_problem(p, &s) != STEM_OK) return 0;
+  if (dtype != STEM_DTYPE_BF16 && dtype != STEM_DTYPE_FP8_E4M3) return 0;
+  return attn_workspace_bytes(s.Hkv, s.R, dtype == STEM_DTYPE_FP8_E4M3);
+}
+
 static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, const void *k,
                        const void *v, const float *q_scale, const float *k_scale,
                        const float *v_scale, const int32_t *block_idx, const int32_t *block_cnt,
-                       int32_t k_cap, float softmax_scale, void *out, float *lse, void *stream,
-                       bool sparse) {
+                       int32_t k_cap, float softmax_scale, void *out, float *lse, void *workspace,
+                       size_t workspace_bytes, void *stream, bool sparse) {
   Shape s;
   int st = check_problem(p, &s);
   if (st != STEM_OK) return st;
@@ -223,6 +230,8 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
     return STEM_ERR_UNSUPPORTED;
   }
   if (sparse && (!block_idx || !block_cnt || k_cap < 1)) return STEM_ERR_INVALID_ARG;
+  const size_t need = attn_workspace_bytes(s.Hkv, s.R, fp8);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return STEM_ERR_WORKSPACE;
 
   AttnLaunch a;
   a.q = q;
@@ -236,12 +245,20 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
   a.k_cap = k_cap;
   a.out = out;
   a.lse = lse;
+  if (fp8) {
+    a.vimg8 = (uint8_t *)workspace;
+    a.vimg16 = (uint16_t *)((uint8_t *)workspace + (size_t)s.Hkv * s.R * kBlock * kHeadDim);
+  } else {
+    a.vimg8 = nullptr;
+    a.vimg16 = (uint16_t *)workspace;
+  }
   a.Hq = s.Hq;
   a.Hkv = s.Hkv;
   a.R = s.R;
   a.T = s.T;
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
   hipStream_t hs = as_stream(stream);
+  if (launch_vprep(a, fp8, hs) != hipSuccess) return STEM_ERR_HIP;
   for (int z0 = 0; z0 < s.B; z0 += kMaxSeqsPerLaunch) {
     const int n = s.B - z0 < kMaxSeqsPerLaunch ? s.B - z0 : kMaxSeqsPerLaunch;
     SeqTable t;
@@ -256,17 +273,18 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
 int stem_bsa_prefill(const stem_problem_t *p, int32_t dtype, const void *q, const void *k,
                      const void *v, const float *q_scale, const float *k_scale,
                      const float *v_scale, const int32_t *block_idx, const int32_t *block_cnt,
-                     int32_t k_cap, float softmax_scale, void *out, float *lse, void *stream) {
+                     int32_t k_cap, float softmax_scale, void *out, float *lse, void *workspace,
+                     size_t workspace_bytes, void *stream) {
   return attn_common(p, dtype, q, k, v, q_scale, k_scale, v_scale, block_idx, block_cnt, k_cap,
-                     softmax_scale, out, lse, stream, true);
+                     softmax_scale, out, lse, workspace, workspace_bytes, stream, true);
 }
 
 int stem_dense_prefill(const stem_problem_t *p, int32_t dtype, const void *q, const void *k,
                        const void *v, const float *q_scale, const float *k_scale,
                        const float *v_scale, float softmax_scale, void *out, float *lse,
-                       void *stream) {
+                       void *workspace, size_t workspace_bytes, void *stream) {
   return attn_common(p, dtype, q, k, v, q_scale, k_scale, v_scale, nullptr, nullptr, 0,
-                     softmax_scale, out, lse, stream, false);
+                     softmax_scale, out, lse, workspace, workspace_bytes, stream, false);
 }
 
 }  // extern "C"

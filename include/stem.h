@@ -138,6 +138,17 @@ int32_t stem_max_kept(const stem_problem_t *p, const double *k_start_host, doubl
                       double alpha, int32_t n_init, int32_t n_window);
 
 /* ---------------------------------------------------------------------------
+ * Workspace of stem_bsa_prefill / stem_dense_prefill: device memory of at
+ * least this many bytes, 256-byte aligned (0 for an invalid problem or
+ * dtype).  Each call first rewrites it with V in the tile layout the
+ * attention kernel loads (per KV head and key block, the 128 x 128 V^T tile;
+ * fp16 for bf16 inputs, e4m3 plus fp16 for fp8 inputs): T * Hkv * d * 2
+ * bytes for bf16, T * Hkv * d * 3 bytes for fp8.  Contents on return are
+ * unspecified; concurrent calls need separate workspaces.
+ * ------------------------------------------------------------------------- */
+size_t stem_attn_workspace_bytes(const stem_problem_t *p, int32_t dtype);
+
+/* ---------------------------------------------------------------------------
  * Stage 3: causal block-sparse attention.  AngelSlim doc §2.3: exact
  * attention on the selected blocks only; youleyou HPC-BSA article §三.3.1: a
  * skipped block is equivalent to all its scores being -inf.
@@ -152,12 +163,18 @@ int32_t stem_max_kept(const stem_problem_t *p, const double *k_start_host, doubl
  * block_idx / block_cnt as produced by stem_schedule_topk (k_cap = its row
  *   stride; entries must be ascending, in [0, I]).
  * out: bf16 [T][Hq][d].  lse: optional fp32 [Hq][T] (natural log), may be NULL.
+ * workspace: see stem_attn_workspace_bytes (STEM_ERR_WORKSPACE if too small).
+ * Precision: Q.K^T in the input type (bf16, or e4m3 with fp32 scales), fp32
+ * accumulation and softmax; P.V with P rounded to fp16 against an exact fp16
+ * copy of V for bf16 inputs (V magnitudes above 65504 saturate), and to e4m3
+ * (as p * 256) for fp8 inputs except in the diagonal block, which uses fp16.
  * ------------------------------------------------------------------------- */
 int stem_bsa_prefill(const stem_problem_t *p, int32_t dtype, const void *q, const void *k,
                      const void *v, const float *q_scale, const float *k_scale,
                      const float *v_scale, const int32_t *block_idx,
                      const int32_t *block_cnt, int32_t k_cap, float softmax_scale,
-                     void *out, float *lse, void *stream);
+                     void *out, float *lse, void *workspace, size_t workspace_bytes,
+                     void *stream);
 
 /* ---------------------------------------------------------------------------
  * Dense causal attention with the same tile kernel (every causal block).
@@ -166,7 +183,7 @@ int stem_bsa_prefill(const stem_problem_t *p, int32_t dtype, const void *q, cons
 int stem_dense_prefill(const stem_problem_t *p, int32_t dtype, const void *q, const void *k,
                        const void *v, const float *q_scale, const float *k_scale,
                        const float *v_scale, float softmax_scale, void *out, float *lse,
-                       void *stream);
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -123,13 +123,21 @@ def test_attention_argument_errors():
     lib = stem.load_library()
     p = stem.Problem([0, 1024], 4, 2)
     f = FAKE
-    assert lib.stem_bsa_prefill(p.ref, 0, f, f, f, None, None, None, None, f, 8, 0.1, f, None, None) == 1
-    assert lib.stem_bsa_prefill(p.ref, 0, f, f, f, f, None, None, f, f, 8, 0.1, f, None, None) == 1
-    assert lib.stem_bsa_prefill(p.ref, 1, f, f, f, None, None, None, f, f, 8, 0.1, f, None, None) == 1
-    assert lib.stem_bsa_prefill(p.ref, 7, f, f, f, None, None, None, f, f, 8, 0.1, f, None, None) == 2
-    assert lib.stem_bsa_prefill(p.ref, 0, f, f, f, None, None, None, f, f, 0, 0.1, f, None, None) == 1
-    assert lib.stem_dense_prefill(p.ref, 0, f, f, f, None, None, None, -1.0, f, None, None) == 1
-    assert lib.stem_dense_prefill(p.ref, 0, None, f, f, None, None, None, 0.1, f, None, None) == 1
+    W = 1 << 30
+    assert lib.stem_bsa_prefill(p.ref, 0, f, f, f, None, None, None, None, f, 8, 0.1, f, None, f, W, None) == 1
+    assert lib.stem_bsa_prefill(p.ref, 0, f, f, f, f, None, None, f, f, 8, 0.1, f, None, f, W, None) == 1
+    assert lib.stem_bsa_prefill(p.ref, 1, f, f, f, None, None, None, f, f, 8, 0.1, f, None, f, W, None) == 1
+    assert lib.stem_bsa_prefill(p.ref, 7, f, f, f, None, None, None, f, f, 8, 0.1, f, None, f, W, None) == 2
+    assert lib.stem_bsa_prefill(p.ref, 0, f, f, f, None, None, None, f, f, 0, 0.1, f, None, f, W, None) == 1
+    assert lib.stem_bsa_prefill(p.ref, 0, f, f, f, None, None, None, f, f, 8, 0.1, f, None, None, W, None) == 4
+    assert lib.stem_bsa_prefill(p.ref, 0, f, f, f, None, None, None, f, f, 8, 0.1, f, None, f, 100, None) == 4
+    assert lib.stem_dense_prefill(p.ref, 0, f, f, f, None, None, None, -1.0, f, None, f, W, None) == 1
+    assert lib.stem_dense_prefill(p.ref, 0, None, f, f, None, None, None, 0.1, f, None, f, W, None) == 1
+    assert lib.stem_dense_prefill(p.ref, 0, f, f, f, None, None, None, 0.1, f, None, ctypes.c_void_p(0x1010),
+                                  W, None) == 4
+    assert stem.stem_attn_workspace_bytes(p, 0) == 2 * 8 * 128 * 128 * 2
+    assert stem.stem_attn_workspace_bytes(p, 1) == 2 * 8 * 128 * 128 * 3
+    assert stem.stem_attn_workspace_bytes(p, 5) == 0
 
 
 def test_package_defaults_match_the_doc_table():
