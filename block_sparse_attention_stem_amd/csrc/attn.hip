@@ -16,9 +16,14 @@
 //    l % 32 in every accumulator: the row max is one cross-half exchange and
 //    the O rescale is a per-lane scalar.
 //  * K and V tiles reach LDS through asynchronous direct loads
-//    (global_load_lds_dwordx4): no staging registers, no staging VALU.  Rows
-//    are XOR-swizzled in 16-byte chunks (chunk c of row r at c ^ (r & 7)) so
-//    the MFMA operand reads of 8 consecutive rows hit 8 different bank groups.
+//    (global_load_lds_dwordx4): no staging registers, no staging VALU.  Each
+//    1 KB instruction fills 64 consecutive 16-byte LDS slots, and each lane
+//    may fetch any global chunk, so tiles are laid out with one pad chunk per
+//    row (rows of 17 chunks for 256-byte rows, 9 for 128-byte rows; a pad
+//    slot re-reads a valid chunk).  Row r then starts 4 (r mod 16) banks
+//    further along the 64-bank LDS, so the 16 lanes served together (16
+//    consecutive rows, same column) never collide, and every operand read of
+//    a lane is one base address plus immediate offsets.
 //  * V^T cannot be produced by a plain copy, so a pre-pass writes each V block
 //    once per call as the exact LDS image: transposed, keys permuted into the
 //    order the S^T accumulators hold them, swizzled, and (bf16 path) converted
@@ -28,6 +33,8 @@
 //    K reads end and its V right after the V reads end, so every load has a
 //    whole compute phase to land; the list is read one entry ahead and the
 //    inner loop never tests whether a block is kept.
+#include <type_traits>
+
 #include "stem_internal.h"
 #include "gfx950_util.h"
 
@@ -63,8 +70,14 @@ __device__ __forceinline__ void block_sync() {
 typedef const __attribute__((address_space(4))) int32_t cint32;
 __device__ __forceinline__ cint32 *as_const(const int32_t *p) { return (cint32 *)p; }
 
-constexpr int kTile16 = kBlock * kHeadDim;        // 16-bit elements in a 128x128 tile (32 KB)
-constexpr int kTile8 = kBlock * kHeadDim;         // bytes in a 128x128 fp8 tile (16 KB)
+// Padded tile images: 128 rows of 17 (16-bit rows) or 9 (8-bit rows) 16-byte
+// chunks; the last chunk of a row is padding.
+constexpr int kRow16 = 136;                        // elements per 16-bit row (272 B)
+constexpr int kRow8 = 144;                         // bytes per 8-bit row
+constexpr int kTile16 = kBlock * kRow16;           // 16-bit elements per tile (34 KB)
+constexpr int kTile8 = kBlock * kRow8;             // bytes per fp8 tile (18 KB)
+constexpr int kSlots16 = kTile16 / 8;              // 16-byte slots per 16-bit tile (2176 = 34 KB)
+constexpr int kSlots8 = kTile8 / 16;               // 16-byte slots per fp8 tile (1152 = 18 KB)
 
 // Key order inside a 16-bit V^T row: lane group x of PV step c reads the
 // 8 contiguous elements 16c + 8x + 4j + r (j, r < 4), which must hold keys
@@ -101,16 +114,17 @@ __global__ __launch_bounds__(256) void vprep_bf16_kernel(const __bf16 *__restric
   uint16_t *out = img + ((size_t)g * R + kb) * kTile16;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    const int d = (tid >> 4) + 16 * p, pch = tid & 15, lch = pch ^ (d & 7);
+    const int d = (tid >> 4) + 16 * p, ch = tid & 15;
     uint32_t w4[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = tile[key_of_pos16(8 * lch + 2 * e) * RS + d];
-      const uint32_t hi = tile[key_of_pos16(8 * lch + 2 * e + 1) * RS + d];
+      const uint32_t lo = tile[key_of_pos16(8 * ch + 2 * e) * RS + d];
+      const uint32_t hi = tile[key_of_pos16(8 * ch + 2 * e + 1) * RS + d];
       w4[e] = lo | (hi << 16);
     }
-    st16(out + d * kHeadDim + 8 * pch, u32x4{w4[0], w4[1], w4[2], w4[3]});
+    st16(out + d * kRow16 + 8 * ch, u32x4{w4[0], w4[1], w4[2], w4[3]});
   }
+  if (tid < kBlock) st16(out + tid * kRow16 + kHeadDim, u32x4{0u, 0u, 0u, 0u});   // pad chunk
 }
 
 // fp8: writes the e4m3 V^T image (16 KB per block) and an fp16 V^T image
@@ -130,30 +144,32 @@ __global__ __launch_bounds__(256) void vprep_fp8_kernel(const uint8_t *__restric
   uint8_t *o8 = img8 + ((size_t)g * R + kb) * kTile8;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    const int d = (tid >> 3) + 32 * p, pch = tid & 7, lch = pch ^ (d & 7);
+    const int d = (tid >> 3) + 32 * p, ch = tid & 7;
     uint32_t w4[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       uint32_t x = 0;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) x |= (uint32_t)tile[key_of_pos8(16 * lch + 4 * e + b) * RS + d] << (8 * b);
+      for (int b = 0; b < 4; ++b) x |= (uint32_t)tile[key_of_pos8(16 * ch + 4 * e + b) * RS + d] << (8 * b);
       w4[e] = x;
     }
-    st16(o8 + d * kHeadDim + 16 * pch, u32x4{w4[0], w4[1], w4[2], w4[3]});
+    st16(o8 + d * kRow8 + 16 * ch, u32x4{w4[0], w4[1], w4[2], w4[3]});
   }
+  if (tid < kBlock) st16(o8 + tid * kRow8 + kHeadDim, u32x4{0u, 0u, 0u, 0u});
   uint16_t *o16 = img16 + ((size_t)g * R + kb) * kTile16;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    const int d = (tid >> 4) + 16 * p, pch = tid & 15, lch = pch ^ (d & 7);
+    const int d = (tid >> 4) + 16 * p, ch = tid & 15;
     uint32_t w4[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float lo = __builtin_amdgcn_cvt_f32_fp8((int)tile[key_of_pos16(8 * lch + 2 * e) * RS + d], 0);
-      const float hi = __builtin_amdgcn_cvt_f32_fp8((int)tile[key_of_pos16(8 * lch + 2 * e + 1) * RS + d], 0);
+      const float lo = __builtin_amdgcn_cvt_f32_fp8((int)tile[key_of_pos16(8 * ch + 2 * e) * RS + d], 0);
+      const float hi = __builtin_amdgcn_cvt_f32_fp8((int)tile[key_of_pos16(8 * ch + 2 * e + 1) * RS + d], 0);
       w4[e] = pack_f16x2(lo, hi);
     }
-    st16(o16 + d * kHeadDim + 8 * pch, u32x4{w4[0], w4[1], w4[2], w4[3]});
+    st16(o16 + d * kRow16 + 8 * ch, u32x4{w4[0], w4[1], w4[2], w4[3]});
   }
+  if (tid < kBlock) st16(o16 + tid * kRow16 + kHeadDim, u32x4{0u, 0u, 0u, 0u});
 }
 
 // ============================================================ work decode
@@ -206,13 +222,12 @@ __device__ __forceinline__ void write_empty(__bf16 *orow, float *lse, int lg) {
 __device__ __forceinline__ float softmax_step(f32x16 (&s)[4], bool diag, int qloc, int lg, float c,
                                               float &m_run, float &l_run) {
   if (diag) {
+    const int lim = qloc - 4 * lg;          // key > qloc  <=>  (key - 4 lg) > lim
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = 32 * tt + 8 * (i >> 2) + 4 * lg + (i & 3);
-        if (key > qloc) s[tt][i] = -INFINITY;
-      }
+      for (int i = 0; i < 16; ++i)
+        s[tt][i] = (32 * tt + 8 * (i >> 2) + (i & 3) > lim) ? -INFINITY : s[tt][i];
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -237,19 +252,50 @@ __device__ __forceinline__ float softmax_step(f32x16 (&s)[4], bool diag, int qlo
 }
 
 // ===================================================================== bf16
-template <bool kSparse>
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a, SeqTable t, int rows) {
-  __shared__ __attribute__((aligned(1024))) uint16_t Ks[kTile16];   // bf16 K, [key][d] swizzled
-  __shared__ __attribute__((aligned(1024))) uint16_t Vs[kTile16];   // fp16 V^T image
+// One workgroup of 8 waves per (query head, query block), one workgroup per
+// CU.  Waves w and w + 4 share a SIMD and the same 32 queries (w & 3); wave w
+// (group 0) takes keys 0-63 of every listed block, wave w + 4 (group 1) keys
+// 64-127, each with its own online softmax, merged once per row.  A group
+// loads only its own halves of the K and V^T tiles.
+//
+// Ping-pong.  A wave alternates an MFMA phase M_b = (P.V of block b-1, then
+// S^T = K Q^T of block b) and a VALU phase X_b = (softmax of block b: mask,
+// max, lazy O rescale, exp2, fp16 packing of P), with a barrier after each.
+// Both groups run the same code, but group 1 passes one extra barrier first,
+// so it stays exactly one phase behind: on every SIMD one wave's exponentials
+// overlap the other wave's MFMAs.
+//
+// Buffers.  Block b's K half sits in K[b % 2] and its V half in V[b % 2]
+// (separate LDS arrays, so the compiler sees that reads never alias loads in
+// flight).  During M_b a group requests K of block b+1 and V of block b;
+// both have the rest of M_b and X_b to land and are awaited before the
+// barrier that opens M_{b+1}.
+//
+// O is rescaled lazily: the running max used for the weights is raised only
+// when a block's max exceeds it by more than 2^8 (weights stay <= 256, exact
+// range for fp16), which skips almost every rescale.
+constexpr float kLazyLog2 = 8.f;
+constexpr int kHalfK = 64 * kRow16;              // K half: 64 keys x 17 chunks (elements)
+constexpr int kRowVh = 72;                       // V^T half row: 64 keys + pad chunk (elements)
+constexpr int kHalfV = kHeadDim * kRowVh;        // V^T half: 128 dims x 9 chunks (elements)
+constexpr uint32_t kBufWord3 = 0x00020000u;      // raw buffer descriptor word 3 (gfx9 dword access)
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lg = lane >> 5, l32 = lane & 31, sw = l32 & 7;
+template <bool kSparse>
+__global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTable t, int rows) {
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[2 * kHalfK];   // bf16 K halves, [key][d]
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[2 * kHalfV];   // fp16 V^T halves, [d][key]
+  __shared__ __attribute__((aligned(1024))) uint16_t K1[2 * kHalfK];
+  __shared__ __attribute__((aligned(1024))) uint16_t V1[2 * kHalfV];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int lg = lane >> 5, l32 = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qw = wv & 3, kh = wv >> 2;
   const AttnItem w = decode_attn(a, t, rows);
-  const uint16_t *kp = (const uint16_t *)a.k;
   const int zrow = t.row[w.z];
   const size_t ztok = (size_t)t.tok[w.z];
   const size_t qtok0 = ztok + (size_t)w.I * kBlock;
-  const int qloc = wave * 32 + l32;
+  const int qloc = qw * 32 + l32;
   const size_t qtok = qtok0 + qloc;
   cint32 *list = kSparse ? as_const(a.idx) + ((size_t)w.h * a.R + w.r) * a.k_cap : nullptr;
   // Lists are trusted to be ascending in [0, I]; counts and ids are still
@@ -259,10 +305,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a, SeqTabl
   __bf16 *orow = (__bf16 *)a.out + (qtok * a.Hq + w.h) * kHeadDim;
   float *lse = a.lse ? a.lse + (size_t)w.h * a.T + qtok : nullptr;
   if (n_blk <= 0) {
-    write_empty(orow, lse, lg);
+    if (kh == 0) write_empty(orow, lse, lg);
     return;
   }
-  auto clampJ = [&](int x) { return x < 0 ? 0 : (x > w.I ? w.I : x); };
+  auto blk = [&](int b) { return kSparse ? (int)(list[b] < 0 ? 0 : (list[b] > w.I ? w.I : list[b])) : b; };
 
   // Q as the B operand: query qloc, head dims 16 ks + 8 lg .. +7
   bf16x8 qf[8];
@@ -272,101 +318,226 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnLaunch a, SeqTabl
     for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(ld16(qrow + 16 * ks));
   }
 
-  // Direct loads: wave w moves 8 KB of each tile, 1 KB per instruction
-  // (4 rows of 256 B); lane i writes LDS bytes 16 i .. 16 i + 15.  Bases are
-  // wave-uniform (scalar registers); each lane adds one fixed offset.  For K,
-  // row r = 32 w + 4 j + (lane >> 4) takes its 16-byte chunk (lane & 15) ^
-  // (r & 7), and r & 7 = (lane >> 4) + 4 (j & 1).
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  const size_t kstride = (size_t)a.Hkv * kHeadDim;
-  const uint32_t koff_even = (lane >> 4) * kstride + 8 * ((lane & 15) ^ (lane >> 4));
-  const uint32_t koff_odd = (lane >> 4) * kstride + 8 * ((lane & 15) ^ ((lane >> 4) + 4));
-  const uint16_t *kbase = kp + ((ztok + 32 * wv) * a.Hkv + w.g) * kHeadDim;
-  const uint16_t *vbase = a.vimg16 + ((size_t)w.g * a.R + zrow) * kTile16 + (8 * wv) * 512;
-  auto issue_k = [&](int J) __attribute__((always_inline)) {
-    const uint16_t *src = kbase + (size_t)J * kBlock * kstride;
+  // Direct loads through raw buffer descriptors rebased per block (32-bit
+  // per-lane offsets, scalar bases).  Load instruction k of a half writes
+  // LDS slots 64 k + lane (16 B each); group wave qw issues k = qw + 4 m.
+  //   K half: 17 loads; slot s -> key row s / 17, chunk s % 17 (chunk 16 is
+  //           the pad and re-reads chunk 0).
+  //   V half: 18 loads; slot s -> dim row s / 9, chunk s % 9 of this half's
+  //           8 image chunks (chunk 8 is the pad and re-reads chunk 0).
+  const uint32_t kstride_b = (uint32_t)a.Hkv * kHeadDim * 2;
+  const int nkk = qw == 0 ? 5 : 4, nkv = qw < 2 ? 5 : 4;
+  uint32_t koff[5], voff[5];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_global_load_lds(src + 4 * j * kstride + ((j & 1) ? koff_odd : koff_even),
-                                       lds_ptr(Ks + (8 * wv + j) * 512), 16, 0, 0);
-  };
-  auto issue_v = [&](int J) __attribute__((always_inline)) {
-    const uint16_t *src = vbase + (size_t)J * kTile16 + lane * 8;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_global_load_lds(src + j * 512, lds_ptr(Vs + (8 * wv + j) * 512), 16, 0, 0);
-  };
-  // Swizzled operand reads: row 32 t + l32 (l32 & 7 = x), logical chunk
-  // 2 k + lg sits at 2 (k ^ (x >> 1)) + (lg ^ (x & 1)); k ^ (x >> 1) only
-  // permutes k's two low bits, so 4 base addresses plus immediate offsets
-  // cover every read.
-  const int x0 = sw & 1, x21 = sw >> 1;
-  const uint16_t *kad[4], *vad[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    kad[b] = &Ks[l32 * kHeadDim + 8 * (lg ^ x0) + 16 * (b ^ x21)];
-    vad[b] = &Vs[l32 * kHeadDim + 8 * (lg ^ x0) + 16 * (b ^ x21)];
+  for (int m = 0; m < 5; ++m) {
+    const int sk = 64 * (qw + 4 * m) + lane;
+    const int rk = sk / 17, ck = sk - 17 * rk;
+    koff[m] = (uint32_t)rk * kstride_b + 16 * (ck < 16 ? ck : 0);
+    const int sv = 64 * (qw + 4 * m) + lane;
+    const int rv = sv / 9, cv = sv - 9 * rv;
+    voff[m] = (uint32_t)(rv * kRow16 * 2 + 16 * (8 * kh + (cv < 8 ? cv : 0)));
   }
+  const char *kbase = (const char *)a.k + ((ztok + 64 * kh) * a.Hkv + w.g) * kHeadDim * 2;
+  const char *vbase = (const char *)(a.vimg16 + ((size_t)w.g * a.R + zrow) * kTile16);
+  // Block ids are wave-uniform; readfirstlane keeps the descriptors in SGPRs.
+  auto issue_k = [&](int J, uint16_t *Kd) __attribute__((always_inline)) {
+    J = __builtin_amdgcn_readfirstlane(J);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(kbase + (size_t)J * kBlock * kstride_b), (short)0, (int)(64 * kstride_b), kBufWord3);
+    uint16_t *d = Kd + kh * kHalfK;
+#pragma unroll
+    for (int m = 0; m < 5; ++m)
+      if (m < nkk) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(d + (qw + 4 * m) * 512), 16, koff[m], 0, 0, 0);
+  };
+  // The loads of one block step: d = 0..4 are K loads m = d of the next
+  // block (a descriptor of size 0 when there is none: no memory is read and
+  // the free buffer gets zeros), d = 5..9 are V loads m = d - 5 of this block.
+  auto k_rsrc = [&](int Jn, bool has_next) __attribute__((always_inline)) {
+    Jn = __builtin_amdgcn_readfirstlane(Jn);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + (size_t)Jn * kBlock * kstride_b), (short)0,
+                                             has_next ? (int)(64 * kstride_b) : 0, kBufWord3);
+  };
+  auto v_rsrc = [&](int J) __attribute__((always_inline)) {
+    J = __builtin_amdgcn_readfirstlane(J);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + (size_t)J * kTile16 * 2), (short)0, kTile16 * 2,
+                                             kBufWord3);
+  };
 
   const float c = a.scale_log2;
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 o[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) o[u] = f32x16{};
+  f32x16 s[2];            // S^T of the current block (this wave's 64 keys)
+  u32x4 pk[4];            // P of the previous block, fp16, one 16-key step each
 
-  // One block of the pipeline.  `issue` is a constant at each call site: the
-  // loop body always prefetches the next block, the peeled last block never
-  // does, so the number of loads in flight is the same on every path (the
-  // compiler's wait bookkeeping then keeps the precise vmcnt(8)).
-  auto step = [&](int J, int Jn, bool issue) __attribute__((always_inline)) {
-    wait_vmcnt<8>();                 // this wave's K of block J has landed (V may be in flight)
-    block_sync();                    // ... and every wave's
-    f32x16 s[4];
+  // MFMA phase: P.V of the previous block (if kPV) from the V^T half in Vp,
+  // then S^T of this block from the K half in Kc, as one stream of MFMAs
+  // whose LDS operand reads run kAhead MFMAs ahead (LDS latency under load
+  // is several MFMA durations).  Consecutive MFMAs use independent
+  // accumulators: P.V steps go (16-key step cc, dim tile u) with u inner,
+  // S^T steps go (head-dim step ks, key tile tt) with tt inner.  The step's
+  // ten direct loads are spread through the stream (one every third MFMA):
+  // issued back to back they stall the wave on the memory issue queue.
+  constexpr int kAhead = 8;
+  auto mfma_phase = [&](auto kPV, const uint16_t *Vp, const uint16_t *Kc, __amdgpu_buffer_rsrc_t rk,
+                        __amdgpu_buffer_rsrc_t rv, uint16_t *Kn, uint16_t *Vc) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(kPV)::value;
+    uint16_t *dk = Kn + kh * kHalfK, *dv = Vc + kh * kHalfV;
+    auto dma = [&](int d) __attribute__((always_inline)) {
+      if (d < 5) {
+        if (d < nkk) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_ptr(dk + (qw + 4 * d) * 512), 16, koff[d], 0, 0, 0);
+      } else {
+        const int m = d - 5;
+        if (m < nkv) __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_ptr(dv + (qw + 4 * m) * 512), 16, voff[m], 0, 0, 0);
+      }
+    };
+    constexpr int i0 = PV ? 0 : 16;
+    const uint16_t *vad = Vp + kh * kHalfV + l32 * kRowVh + 8 * lg;
+    const uint16_t *kad = Kc + kh * kHalfK + l32 * kRow16 + 8 * lg;
+    auto rd = [&](int i) __attribute__((always_inline)) {
+      return i < 16 ? ld16(vad + 32 * kRowVh * (i & 3) + 16 * (i >> 2))
+                    : ld16(kad + 32 * kRow16 * ((i - 16) & 1) + 16 * ((i - 16) >> 1));
+    };
+    u32x4 r[32];
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt) {
-      s[tt] = f32x16{};
+    for (int i = i0; i < i0 + kAhead; ++i) r[i] = rd(i);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-        s[tt] = mfma_bf16_32x32x16(as_bf16x8(ld16(kad[ks & 3] + 32 * kHeadDim * tt + 64 * (ks >> 2))), qf[ks],
-                                   s[tt]);
+    for (int i = i0; i < 32; ++i) {
+      if (i + kAhead < 32) r[i + kAhead] = rd(i + kAhead);
+      if (PV ? (i % 3 == 1 && i < 30) : (i - 16 < 10)) dma(PV ? i / 3 : i - 16);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i < 16) {
+        o[i & 3] = mfma_f16_32x32x16(as_f16x8(r[i]), as_f16x8(pk[i >> 2]), o[i & 3]);
+      } else {
+        const int tt = (i - 16) & 1, ks = (i - 16) >> 1;
+        s[tt] = mfma_bf16_32x32x16(as_bf16x8(r[i]), qf[ks], ks == 0 ? f32x16{} : s[tt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    const float alpha = softmax_step(s, J == w.I, qloc, lg, c, m_run, l_run);
-    if (__any(alpha != 1.f)) {
+  };
+  // P.V of the last block (no S^T after it).
+  auto pv_last = [&](const uint16_t *Vp) __attribute__((always_inline)) {
+    const uint16_t *vad = Vp + kh * kHalfV + l32 * kRowVh + 8 * lg;
+    u32x4 r[16];
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) r[i] = ld16(vad + 32 * kRowVh * (i & 3) + 16 * (i >> 2));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (i + kAhead < 16) r[i + kAhead] = ld16(vad + 32 * kRowVh * ((i + kAhead) & 3) + 16 * ((i + kAhead) >> 2));
+      __builtin_amdgcn_sched_barrier(0);
+      o[i & 3] = mfma_f16_32x32x16(as_f16x8(r[i]), as_f16x8(pk[i >> 2]), o[i & 3]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // Softmax of the block whose S^T is in s (lane: 32 of the query's 64 keys
+  // in this half).  A query can see no key at all in this half (diagonal
+  // block, keys 64-127, queries < 64): its max stays -inf, alpha stays 1 and
+  // the exponent offset is 0, so every weight is 0.
+  auto softmax = [&](bool diag) __attribute__((always_inline)) {
+    if (diag) {
+      const int lim = qloc - 64 * kh - 4 * lg;        // key > qloc  <=>  local key offset > lim
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          s[tt][i] = (32 * tt + 8 * (i >> 2) + (i & 3) > lim) ? -INFINITY : s[tt][i];
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[tt][i]);
+    mx = wave_max_xor32(mx) * c;
+    if (__any(mx > m_run + kLazyLog2)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new > m_run ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[u][i] *= alpha;
     }
-    wait_vmcnt<0>();                 // V of block J has landed
-    block_sync();                    // every wave: V landed, K reads done
-    if (issue) issue_k(Jn);
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    float psum = 0.f;
 #pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[tt][i] = __builtin_amdgcn_exp2f(fmaf(s[tt][i], c, -m_use));
+        psum += s[tt][i];
+      }
+    l_run += psum;
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
       const int tt = cc >> 1, j0 = 8 * (cc & 1);
-      const u32x4 v4 = {pack_f16x2(s[tt][j0 + 0], s[tt][j0 + 1]), pack_f16x2(s[tt][j0 + 2], s[tt][j0 + 3]),
-                        pack_f16x2(s[tt][j0 + 4], s[tt][j0 + 5]), pack_f16x2(s[tt][j0 + 6], s[tt][j0 + 7])};
-      const f16x8 pk = as_f16x8(v4);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        o[u] = mfma_f16_32x32x16(as_f16x8(ld16(vad[cc & 3] + 32 * kHeadDim * u + 64 * (cc >> 2))), pk, o[u]);
+      pk[cc] = u32x4{pack_f16x2(s[tt][j0 + 0], s[tt][j0 + 1]), pack_f16x2(s[tt][j0 + 2], s[tt][j0 + 3]),
+                     pack_f16x2(s[tt][j0 + 4], s[tt][j0 + 5]), pack_f16x2(s[tt][j0 + 6], s[tt][j0 + 7])};
     }
-    block_sync();                    // every wave is done reading V
-    if (issue) issue_v(Jn);
   };
 
-  int J = kSparse ? clampJ(list[0]) : 0;
-  issue_k(J);
-  issue_v(J);
-  for (int b = 0; b + 1 < n_blk; ++b) {
-    const int Jn = kSparse ? clampJ(list[b + 1]) : b + 1;
-    step(J, Jn, true);
+  // Block b: [wait, barrier, loads for b+1, M_b, barrier, X_b].  Block b
+  // uses K[b % 2] and V[b % 2]; P.V of block b-1 reads V[(b-1) % 2].
+  auto step = [&](auto kPV, int b, int &J, const uint16_t *Kc, const uint16_t *Vp, uint16_t *Kn, uint16_t *Vc)
+                  __attribute__((always_inline)) {
+    const int Jn = b + 1 < n_blk ? blk(b + 1) : 0;
+    wait_vmcnt<0>();                 // this wave's K of b and V of b-1 have landed
+    block_sync();                    // ... the whole group's too; Kn and Vc are free
+    mfma_phase(kPV, Vp, Kc, k_rsrc(Jn, b + 1 < n_blk), v_rsrc(J), Kn, Vc);
+    block_sync();
+    softmax(J == w.I);
     J = Jn;
-  }
-  step(J, 0, false);
+  };
+  using NoPV = std::integral_constant<bool, false>;
+  using WithPV = std::integral_constant<bool, true>;
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  write_out(orow, o, 1.f / l_tot, lg);
-  if (lse && lg == 0) *lse = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+  int J = blk(0);
+  issue_k(J, K0);
+  if (kh == 1) block_sync();         // group 1 runs one phase behind
+  step(NoPV{}, 0, J, K0, V1, K1, V0);
+  int b = 1;
+  while (b < n_blk) {
+    step(WithPV{}, b, J, K1, V0, K0, V1);
+    if (++b == n_blk) break;
+    step(WithPV{}, b, J, K0, V1, K1, V0);
+    ++b;
+  }
+  // P.V of the last block, from V[(n_blk - 1) % 2]; every load has landed
+  wait_vmcnt<0>();
+  block_sync();
+  pv_last((n_blk & 1) ? V0 : V1);
+  if (kh == 0) block_sync();         // realign the groups
+
+  // merge the two key halves: waves 4-7 hand (O, m, l) to waves 0-3 through LDS
+  block_sync();
+  float *xch = (float *)(qw < 2 ? K0 : K1) + (qw & 1) * (66 * 64);
+  if (kh == 1) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xch[(16 * u + i) * 64 + lane] = o[u][i];
+    xch[64 * 64 + lane] = m_run;
+    xch[65 * 64 + lane] = l_run;
+  }
+  block_sync();
+  if (kh == 0) {
+    // the merged max is finite: the key equal to the query is visible in one half
+    const float m1 = xch[64 * 64 + lane], l1 = xch[65 * 64 + lane];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
+    const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
+    float l = l_run * a0 + l1 * a1;
+    l += __shfl_xor(l, 32, 64);
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[u][i] = (o[u][i] * a0 + xch[(16 * u + i) * 64 + lane] * a1) * inv;
+    write_out(orow, o, 1.f, lg);
+    if (lse && lg == 0) *lse = (m + __log2f(l)) * 0.69314718055994531f;
+  }
 }
 
 // ====================================================================== fp8
@@ -387,8 +558,8 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
 
 template <bool kSparse>
 __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable t, int rows) {
-  __shared__ __attribute__((aligned(1024))) uint8_t Ks[kTile8];      // e4m3 K, [key][d] swizzled
-  __shared__ __attribute__((aligned(1024))) uint8_t Vs[kTile8];      // e4m3 V^T image
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks[kTile8];      // e4m3 K, [key][d], padded rows
+  __shared__ __attribute__((aligned(1024))) uint8_t Vs[kTile8];      // e4m3 V^T image, padded rows
   __shared__ __attribute__((aligned(1024))) uint16_t Vh[kTile16];    // fp16 V^T image (diagonal)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -422,49 +593,48 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
   }
   const float cq = a.q_scale[(size_t)w.r * a.Hq + w.h] * a.scale_log2;
 
-  // Direct loads as in the bf16 kernel.  K rows are 128 B: row r = 32 w +
-  // 8 j + (lane >> 3) takes chunk (lane & 7) ^ (r & 7) with r & 7 = lane >> 3.
+  // Direct loads as in the bf16 kernel.  An fp8 tile is 18 instructions
+  // (slot s = 64 k + lane holds chunk s % 9 of row s / 9; chunk 8 is the pad),
+  // 5 for waves 0-1 and 4 for waves 2-3; the fp16 diagonal image is 34.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int nk8 = wv < 2 ? 5 : 4, nk16 = wv < 2 ? 9 : 8;
   const size_t kstride = (size_t)a.Hkv * kHeadDim;
-  const uint32_t koff = (lane >> 3) * kstride + 16 * ((lane & 7) ^ (lane >> 3));
-  const uint8_t *kbase = kp + ((ztok + 32 * wv) * a.Hkv + w.g) * kHeadDim;
-  const uint8_t *v8base = a.vimg8 + ((size_t)w.g * a.R + zrow) * kTile8 + (4 * wv) * 1024;
-  const uint16_t *v16base = a.vimg16 + ((size_t)w.g * a.R + zrow) * kTile16 + (8 * wv) * 512;
-  auto issue_k = [&](int J) __attribute__((always_inline)) {
-    const uint8_t *src = kbase + (size_t)J * kBlock * kstride + koff;
+  uint32_t koff[5];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_global_load_lds(src + 8 * j * kstride, lds_ptr(Ks + (4 * wv + j) * 1024), 16, 0, 0);
+  for (int m = 0; m < 5; ++m) {
+    const int sl = 64 * (wv + 4 * m) + lane;
+    const int r = sl / 9, ch = sl - 9 * (sl / 9);
+    koff[m] = (uint32_t)(r * kstride + 16 * (ch < 8 ? ch : 0));
+  }
+  const uint8_t *kbase = kp + (ztok * a.Hkv + w.g) * kHeadDim;
+  const uint8_t *v8base = a.vimg8 + ((size_t)w.g * a.R + zrow) * kTile8 + lane * 16;
+  const uint16_t *v16base = a.vimg16 + ((size_t)w.g * a.R + zrow) * kTile16 + lane * 8;
+  auto issue_k = [&](int J) __attribute__((always_inline)) {
+    const uint8_t *src = kbase + (size_t)J * kBlock * kstride;
+#pragma unroll
+    for (int m = 0; m < 5; ++m)
+      if (m < nk8) __builtin_amdgcn_global_load_lds(src + koff[m], lds_ptr(Ks + (wv + 4 * m) * 1024), 16, 0, 0);
   };
   auto issue_v8 = [&](int J) __attribute__((always_inline)) {
-    const uint8_t *src = v8base + (size_t)J * kTile8 + lane * 16;
+    const uint8_t *src = v8base + (size_t)J * kTile8;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_global_load_lds(src + j * 1024, lds_ptr(Vs + (4 * wv + j) * 1024), 16, 0, 0);
+    for (int m = 0; m < 5; ++m)
+      if (m < nk8)
+        __builtin_amdgcn_global_load_lds(src + (wv + 4 * m) * 1024, lds_ptr(Vs + (wv + 4 * m) * 1024), 16, 0, 0);
   };
   auto issue_v16 = [&](int J) __attribute__((always_inline)) {
-    const uint16_t *src = v16base + (size_t)J * kTile16 + lane * 8;
+    const uint16_t *src = v16base + (size_t)J * kTile16;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      __builtin_amdgcn_global_load_lds(src + j * 512, lds_ptr(Vh + (8 * wv + j) * 512), 16, 0, 0);
+    for (int m = 0; m < 9; ++m)
+      if (m < nk16)
+        __builtin_amdgcn_global_load_lds(src + (wv + 4 * m) * 512, lds_ptr(Vh + (wv + 4 * m) * 512), 16, 0, 0);
   };
-  // Swizzled reads of 128-byte rows: logical chunk 4 k + 2 lg + e sits at
-  // 4 (k ^ x2) + 2 (lg ^ x1) + (e ^ x0) for x = l32 & 7.
-  const int x0 = sw & 1, x1 = (sw >> 1) & 1, x2 = sw >> 2;
-  const uint8_t *k8ad[2][2], *v8ad[2][2];
-#pragma unroll
-  for (int k = 0; k < 2; ++k)
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int ch = 4 * (k ^ x2) + 2 * (lg ^ x1) + (e ^ x0);
-      k8ad[k][e] = &Ks[l32 * kHeadDim + 16 * ch];
-      v8ad[k][e] = &Vs[l32 * kHeadDim + 16 * ch];
-    }
-  const uint16_t *vhad[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) vhad[b] = &Vh[l32 * kHeadDim + 8 * (lg ^ x0) + 16 * (b ^ (sw >> 1))];
-  auto ld32 = [](const uint8_t *lo_p, const uint8_t *hi_p) __attribute__((always_inline)) {
-    const u32x4 lo = ld16(lo_p), hi = ld16(hi_p);
+  // Operand reads: 32 bytes = chunks 4 k + 2 lg and +1 of row 32 t + l32.
+  const uint8_t *k8ad = &Ks[l32 * kRow8 + 32 * lg];
+  const uint8_t *v8ad = &Vs[l32 * kRow8 + 32 * lg];
+  const uint16_t *vhad = &Vh[l32 * kRow16 + 8 * lg];
+  auto ld32 = [](const uint8_t *p) __attribute__((always_inline)) {
+    const u32x4 lo = ld16(p), hi = ld16(p + 16);
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
 
@@ -489,7 +659,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
       s[tt] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
-        s[tt] = mfma_fp8_32x32x64(ld32(k8ad[ks][0] + 4096 * tt, k8ad[ks][1] + 4096 * tt), qf[ks], s[tt]);
+        s[tt] = mfma_fp8_32x32x64(ld32(k8ad + 32 * kRow8 * tt + 64 * ks), qf[ks], s[tt]);
     }
     const float alpha = softmax_step(s, diag, qloc, lg, c, m_run, l_run);
     const float f = alpha * (vs_run / vs);
@@ -515,7 +685,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
           }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          o[u] = mfma_fp8_32x32x64(ld32(v8ad[cc][0] + 4096 * u, v8ad[cc][1] + 4096 * u), pk, o[u]);
+          o[u] = mfma_fp8_32x32x64(ld32(v8ad + 32 * kRow8 * u + 64 * cc), pk, o[u]);
       }
     } else {
 #pragma unroll
@@ -528,7 +698,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
         const f16x8 pk = as_f16x8(v4);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          o[u] = mfma_f16_32x32x16(as_f16x8(ld16(vhad[cc & 3] + 32 * kHeadDim * u + 64 * (cc >> 2))), pk, o[u]);
+          o[u] = mfma_f16_32x32x16(as_f16x8(ld16(vhad + 32 * kRow16 * u + 16 * cc)), pk, o[u]);
       }
     }
     block_sync();
@@ -574,6 +744,7 @@ size_t attn_workspace_bytes(int Hkv, int R, bool fp8) {
   const size_t per_block = fp8 ? (size_t)kTile8 + 2 * (size_t)kTile16 : 2 * (size_t)kTile16;
   return (size_t)Hkv * R * per_block;
 }
+size_t attn_workspace_img16_offset(int Hkv, int R) { return (size_t)Hkv * R * kTile8; }
 
 hipError_t launch_vprep(const AttnLaunch &a, bool fp8, hipStream_t s) {
   const dim3 grid(a.R, a.Hkv);
@@ -587,13 +758,13 @@ hipError_t launch_vprep(const AttnLaunch &a, bool fp8, hipStream_t s) {
 
 hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows, bool sparse, bool fp8,
                        hipStream_t s) {
-  const dim3 grid(rows * a.Hq), block(256);
+  const dim3 grid(rows * a.Hq);
   if (fp8) {
-    if (sparse) hipLaunchKernelGGL(attn_fp8_kernel<true>, grid, block, 0, s, a, t, rows);
-    else hipLaunchKernelGGL(attn_fp8_kernel<false>, grid, block, 0, s, a, t, rows);
+    if (sparse) hipLaunchKernelGGL(attn_fp8_kernel<true>, grid, dim3(256), 0, s, a, t, rows);
+    else hipLaunchKernelGGL(attn_fp8_kernel<false>, grid, dim3(256), 0, s, a, t, rows);
   } else {
-    if (sparse) hipLaunchKernelGGL(attn_bf16_kernel<true>, grid, block, 0, s, a, t, rows);
-    else hipLaunchKernelGGL(attn_bf16_kernel<false>, grid, block, 0, s, a, t, rows);
+    if (sparse) hipLaunchKernelGGL(attn_bf16_kernel<true>, grid, dim3(512), 0, s, a, t, rows);
+    else hipLaunchKernelGGL(attn_bf16_kernel<false>, grid, dim3(512), 0, s, a, t, rows);
   }
   return hipGetLastError();
 }

@@ -247,7 +247,7 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
   a.lse = lse;
   if (fp8) {
     a.vimg8 = (uint8_t *)workspace;
-    a.vimg16 = (uint16_t *)((uint8_t *)workspace + (size_t)s.Hkv * s.R * kBlock * kHeadDim);
+    a.vimg16 = (uint16_t *)((uint8_t *)workspace + attn_workspace_img16_offset(s.Hkv, s.R));
   } else {
     a.vimg8 = nullptr;
     a.vimg16 = (uint16_t *)workspace;

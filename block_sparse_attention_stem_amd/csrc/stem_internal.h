@@ -110,12 +110,13 @@ struct AttnLaunch {
   int32_t k_cap;
   void *out;
   float *lse;
-  uint16_t *vimg16;              // workspace: fp16 V^T tile images [Hkv][R][128*128]
-  uint8_t *vimg8;                // workspace (fp8 only): e4m3 V^T tile images [Hkv][R][128*128]
+  uint16_t *vimg16;              // workspace: fp16 V^T tile images [Hkv][R][128 rows x 136]
+  uint8_t *vimg8;                // workspace (fp8 only): e4m3 V^T tile images [Hkv][R][128 x 144 B]
   int32_t Hq, Hkv, R, T;
   float scale_log2;              // softmax_scale * log2(e)
 };
 size_t attn_workspace_bytes(int Hkv, int R, bool fp8);
+size_t attn_workspace_img16_offset(int Hkv, int R);
 hipError_t launch_vprep(const AttnLaunch &a, bool fp8, hipStream_t s);
 hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows_in_launch,
                        bool sparse, bool fp8, hipStream_t s);

@@ -141,10 +141,11 @@ int32_t stem_max_kept(const stem_problem_t *p, const double *k_start_host, doubl
  * Workspace of stem_bsa_prefill / stem_dense_prefill: device memory of at
  * least this many bytes, 256-byte aligned (0 for an invalid problem or
  * dtype).  Each call first rewrites it with V in the tile layout the
- * attention kernel loads (per KV head and key block, the 128 x 128 V^T tile;
- * fp16 for bf16 inputs, e4m3 plus fp16 for fp8 inputs): T * Hkv * d * 2
- * bytes for bf16, T * Hkv * d * 3 bytes for fp8.  Contents on return are
- * unspecified; concurrent calls need separate workspaces.
+ * attention kernel loads (per KV head and key block, the 128 x 128 V^T tile
+ * with one 16-byte pad chunk per row; fp16 for bf16 inputs, e4m3 plus fp16
+ * for fp8 inputs): T * Hkv * 272 bytes for bf16, T * Hkv * 416 bytes for
+ * fp8 (d = 128).  Contents on return are unspecified; concurrent calls need
+ * separate workspaces.
  * ------------------------------------------------------------------------- */
 size_t stem_attn_workspace_bytes(const stem_problem_t *p, int32_t dtype);
 

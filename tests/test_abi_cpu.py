@@ -135,8 +135,8 @@ def test_attention_argument_errors():
     assert lib.stem_dense_prefill(p.ref, 0, None, f, f, None, None, None, 0.1, f, None, f, W, None) == 1
     assert lib.stem_dense_prefill(p.ref, 0, f, f, f, None, None, None, 0.1, f, None, ctypes.c_void_p(0x1010),
                                   W, None) == 4
-    assert stem.stem_attn_workspace_bytes(p, 0) == 2 * 8 * 128 * 128 * 2
-    assert stem.stem_attn_workspace_bytes(p, 1) == 2 * 8 * 128 * 128 * 3
+    assert stem.stem_attn_workspace_bytes(p, 0) == 1024 * 2 * 272
+    assert stem.stem_attn_workspace_bytes(p, 1) == 1024 * 2 * 416
     assert stem.stem_attn_workspace_bytes(p, 5) == 0
 
 
