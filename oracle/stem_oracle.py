@@ -133,8 +133,8 @@ def strided_scores(q_seq: np.ndarray, k_seq: np.ndarray, stride: int, scale: flo
     n = L // stride
     if row1 < 0:
         row1 = n
-    qr = q_seq[row0 * stride:row1 * stride].reshape(row1 - row0, stride * d)
-    kr = k_seq[:row1 * stride].reshape(row1, stride, d)[:, ::-1, :].reshape(row1, stride * d)
+    qr = q_seq[row0 * stride:row1 * stride].astype(np.float64).reshape(row1 - row0, stride * d)
+    kr = k_seq[:row1 * stride].astype(np.float64).reshape(row1, stride, d)[:, ::-1, :].reshape(row1, stride * d)
     A = (qr @ kr.T) * scale
     i = np.arange(row0, row1)[:, None]
     j = np.arange(row1)[None, :]
@@ -145,13 +145,14 @@ def strided_scores(q_seq: np.ndarray, k_seq: np.ndarray, stride: int, scale: flo
 def block_scores(q: np.ndarray, k: np.ndarray, bonus: np.ndarray, cu_seqlens: Sequence[int],
                  num_q_heads: int, num_kv_heads: int, block_size: int = 128, stride: int = 8,
                  chunk_size: int = 2048, norm: float = 1.0,
-                 heads: Sequence[int] = None) -> np.ndarray:
+                 heads: Sequence[int] = None, rows: Sequence[int] = None) -> np.ndarray:
     """S[h][global q block][J] (fp32) = max-pooled strided score + bonus[kv(h)][J].
 
     Entries with J > I or J >= nb of the sequence are -inf.  The query axis is
     processed `chunk_size` tokens at a time, as the scoring stage does; the
     chunk width changes the memory footprint only, never a value.
-    `heads` restricts the computation to a subset of query heads (others stay -inf).
+    `heads` restricts the computation to a subset of query heads and `rows` to
+    a subset of global query-block rows (everything else stays -inf).
     """
     T, _, d = q.shape
     m = block_size // stride
@@ -162,6 +163,7 @@ def block_scores(q: np.ndarray, k: np.ndarray, bonus: np.ndarray, cu_seqlens: Se
     scale = 1.0 / (math.sqrt(d) * stride * norm)
     group = num_q_heads // num_kv_heads
     hs = range(num_q_heads) if heads is None else heads
+    want = None if rows is None else set(int(r) for r in rows)
     r0 = 0
     for (a, b), nb in zip(seqs, nbs):
         for h in hs:
@@ -169,11 +171,15 @@ def block_scores(q: np.ndarray, k: np.ndarray, bonus: np.ndarray, cu_seqlens: Se
             qs, ks = q[a:b, h, :], k[a:b, g, :]
             for c0 in range(0, b - a, chunk_size):
                 c1 = min(c0 + chunk_size, b - a)
-                A = strided_scores(qs, ks, stride, scale, c0 // stride, c1 // stride)
                 I0, I1 = c0 // block_size, c1 // block_size
+                if want is not None and not any(r0 + I in want for I in range(I0, I1)):
+                    continue
+                A = strided_scores(qs, ks, stride, scale, c0 // stride, c1 // stride)
                 ncol = A.shape[1]
                 pooled = A.reshape(I1 - I0, m, ncol // m, m).max(axis=(1, 3))   # [I][J]
                 for I in range(I0, I1):
+                    if want is not None and r0 + I not in want:
+                        continue
                     row = pooled[I - I0, :I + 1] + bonus[g, a // block_size:a // block_size + I + 1]
                     S[h, r0 + I, :I + 1] = row.astype(np.float32)
         r0 += nb

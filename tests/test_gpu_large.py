@@ -1,0 +1,177 @@
+"""GPU parity at the full workload sizes: 32K and 128K bf16 layers and the
+128K fp8 varlen layer.
+
+The GPU runs every stage on the whole workload through the C ABI, with the
+entry points, arguments and preallocated workspaces the benchmark times.
+The oracle then checks, at sizes it can afford:
+  * block scores on sampled (head, row) pairs, every key block of each row;
+  * every list of every head and row, selected by the oracle from the GPU's
+    own fp32 scores (bit-exact);
+  * attention output and LSE on sampled (head, row) pairs, on the GPU's lists;
+  * dense attention on sampled heads and query ranges.
+The oracle is fed head subsets (whole GQA groups) so its fp64 copies stay a
+few GB; a subset keeps each query head with its own KV head.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_stem_amd as stem
+import oracle as O
+import stem_synth as S
+from gpu_common import (BF16_MAX_ABS, BF16_MEAN_REL, FP8_MAX_ABS, check_lse, check_out,
+                        check_scores, dev, lists_equal, note, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 1.0 / math.sqrt(128.0)
+HS = [0, 1, 2, 3, 12, 13, 14, 15, 28, 29, 30, 31]    # query heads of KV groups 0, 3, 7
+KS = [0, 3, 7]
+
+
+def _subset64(q, k, v):
+    return (q[:, HS].to(torch.float64).numpy(), k[:, KS].to(torch.float64).numpy(),
+            v[:, KS].to(torch.float64).numpy())
+
+
+def _sample_rows(w):
+    """First, second, middle and last q-block rows of every sequence."""
+    rows, r0 = [], 0
+    for L in w.seqlens:
+        nb = L // 128
+        rows += sorted({r0, r0 + 1, r0 + nb // 2, r0 + nb - 1})
+        r0 += nb
+    return rows
+
+
+def _gather_rows(x, rows):
+    """x [T][Hq][d] on the GPU -> {(h_sub, r): [128][d] float64} for h in HS."""
+    out = {}
+    for hi, h in enumerate(HS):
+        for r in rows:
+            out[(hi, r)] = x[r * 128:(r + 1) * 128, h, :].to(torch.float64).cpu().numpy()
+    return out
+
+
+def _run(w, fp8):
+    note(f"[{w.name}] generating T={w.total_tokens} Hq={w.num_q_heads} Hkv={w.num_kv_heads}")
+    q, k, v = S.make_workload_qkv(w)
+    p = stem.Problem(w.cu_seqlens, w.num_q_heads, w.num_kv_heads)
+    qd, kd, vd = to_dev(q, k, v)
+    ws = torch.empty(stem.stem_score_workspace_bytes(p), dtype=torch.uint8, device=dev())
+    scores = torch.empty((p.Hq, p.R, p.max_nb), dtype=torch.float32, device=dev())
+    kcap = stem.stem_max_kept(p, w.k_start, w.mu, w.alpha, w.n_init, w.n_window)
+    idx = torch.empty((p.Hq, p.R, kcap), dtype=torch.int32, device=dev())
+    cnt = torch.empty((p.Hq, p.R), dtype=torch.int32, device=dev())
+    note(f"[{w.name}] score + schedule (k_cap {kcap})")
+    stem.stem_score(p, qd, kd, vd, w.stride, w.chunk_size, w.norm, w.beta, scores, ws)
+    stem.stem_schedule_topk(p, scores, w.k_start, w.mu, w.alpha, w.n_init, w.n_window, kcap, idx, cnt)
+    dt = stem.STEM_DTYPE_FP8_E4M3 if fp8 else stem.STEM_DTYPE_BF16
+    aws = torch.empty(stem.stem_attn_workspace_bytes(p, dt), dtype=torch.uint8, device=dev())
+    out = torch.empty((p.T, p.Hq, p.d), dtype=torch.bfloat16, device=dev())
+    dout = torch.empty_like(out)
+    lse = torch.empty((p.Hq, p.T), dtype=torch.float32, device=dev())
+    scales = None
+    if fp8:
+        # the harness quantiser: per (128-token block, head) scale amax / 448
+        (q8, qs), (k8, ks), (v8, vs) = (S.quantize_e4m3_per_block(t, w.seqlens) for t in (q, k, v))
+        qa, ka, va = to_dev(q8, k8, v8)
+        scales = to_dev(qs, ks, vs)
+        # the oracle sees the dequantised values of the same codes
+        hq, hk, hv = (O.dequantize_blocks(c.numpy(), s.numpy(), 128) for c, s in
+                      ((q8[:, HS], qs[:, HS]), (k8[:, KS], ks[:, KS]), (v8[:, KS], vs[:, KS])))
+        ref_inputs = (hq, hk, hv)
+    else:
+        qa, ka, va = qd, kd, vd
+        ref_inputs = None
+    note(f"[{w.name}] {'fp8' if fp8 else 'bf16'} block-sparse and dense attention")
+    stem.stem_bsa_prefill(p, qa, ka, va, idx, cnt, SCALE, scales=scales, out=out, lse=lse, workspace=aws)
+    stem.stem_dense_prefill(p, qa, ka, va, SCALE, scales=scales, out=dout, workspace=aws)
+    torch.cuda.synchronize()
+    rows = _sample_rows(w)
+    res = dict(w=w, p=p, kcap=kcap, rows=rows,
+               scores=scores.cpu().numpy(), idx=idx.cpu().numpy(), cnt=cnt.cpu().numpy(),
+               out=_gather_rows(out, rows), dout=_gather_rows(dout, rows),
+               lse={(hi, r): lse[h, r * 128:(r + 1) * 128].to(torch.float64).cpu().numpy()
+                    for hi, h in enumerate(HS) for r in rows})
+    del qd, kd, vd, out, dout, lse, scores, idx, cnt, aws, ws
+    torch.cuda.empty_cache()
+    bf = _subset64(q, k, v)
+    res["bf16_ref_inputs"] = bf
+    res["attn_ref_inputs"] = ref_inputs if fp8 else bf
+    return res
+
+
+@pytest.fixture(scope="module", params=["cfg2_n32k", "cfg3_n128k", "fp8_layer5"])
+def big(request):
+    if request.param == "fp8_layer5":
+        return _run(S.fp8_workload(5), fp8=True)
+    return _run(S.CONFIGS[request.param], fp8=False)
+
+
+def test_scores_on_sampled_rows(big):
+    w, rows = big["w"], big["rows"]
+    qs, ks, vs = big["bf16_ref_inputs"]
+    bonus = O.value_bonus(vs, w.cu_seqlens, 128, w.beta)
+    # chunk width 128 changes no value (pinned on the CPU) and keeps each row cheap
+    ref = O.block_scores(qs, ks, bonus, w.cu_seqlens, len(HS), len(KS), 128, w.stride, 128, w.norm,
+                         rows=rows)
+    gpu = big["scores"][HS][:, rows]
+    check_scores(gpu, ref[:, rows], f"{w.name} {len(HS)} heads x {len(rows)} rows")
+
+
+def test_every_list_bit_exact(big):
+    w = big["w"]
+    ri, rc = O.schedule_topk(big["scores"], w.cu_seqlens, w.k_start, w.mu, w.alpha, w.n_init,
+                             w.n_window, big["kcap"])
+    note(f"  lists {w.name}: {rc.size} rows, {int(rc.sum())} kept blocks")
+    lists_equal(big["idx"], big["cnt"], ri, rc, w.name)
+
+
+def _compare_rows(big, ref_o, ref_lse, gpu_rows, gpu_lse, bar, where):
+    rows = big["rows"]
+    g = np.stack([gpu_rows[(hi, r)] for hi in range(len(HS)) for r in rows])
+    rr = np.stack([ref_o[r * 128:(r + 1) * 128, hi, :] for hi in range(len(HS)) for r in rows])
+    check_out(g, rr, bar[0], bar[1], where)
+    if gpu_lse is not None:
+        gl = np.stack([gpu_lse[(hi, r)] for hi in range(len(HS)) for r in rows])
+        rl = np.stack([ref_lse[hi, r * 128:(r + 1) * 128] for hi in range(len(HS)) for r in rows])
+        check_lse(gl, rl, where)
+
+
+def test_block_sparse_attention_on_sampled_rows(big):
+    w = big["w"]
+    fp8 = w.fp8
+    qs, ks, vs = big["attn_ref_inputs"]
+    idx_sub, cnt_sub = big["idx"][HS], big["cnt"][HS]
+    pairs = [(hi, r) for hi in range(len(HS)) for r in big["rows"]]
+    ro, rl = O.block_sparse_attention(qs, ks, vs, idx_sub, cnt_sub, w.cu_seqlens, len(HS), len(KS),
+                                      SCALE, rows=pairs)
+    bar = (FP8_MAX_ABS, None) if fp8 else (BF16_MAX_ABS, BF16_MEAN_REL)
+    _compare_rows(big, ro, rl, big["out"], big["lse"], bar, f"{w.name} bsa {len(pairs)} rows")
+
+
+def test_dense_attention_on_sampled_rows(big):
+    w = big["w"]
+    fp8 = w.fp8
+    qs, ks, vs = big["attn_ref_inputs"]
+    rows = big["rows"]
+    # one head per sampled KV group: a middle row (the last row of the first
+    # sequence when packed) and the last row overall
+    checks = [(0, rows[2] if len(w.seqlens) == 1 else rows[3]), (6, rows[-1]), (11, rows[-1])]
+    seq_start = {}
+    r0 = 0
+    for z, L in enumerate(w.seqlens):
+        for I in range(L // 128):
+            seq_start[r0 + I] = (w.cu_seqlens[z], I)
+        r0 += L // 128
+    bar = (FP8_MAX_ABS, None) if fp8 else (BF16_MAX_ABS, BF16_MEAN_REL)
+    for hi, r in checks:
+        a, I = seq_start[r]
+        t0 = I * 128
+        ro, _ = O.dense_causal_attention(qs, ks, vs, w.cu_seqlens, len(HS), len(KS), SCALE,
+                                         heads=[hi], q_range=(t0, t0 + 128))
+        check_out(big["dout"][(hi, r)], ro[a + t0:a + t0 + 128, hi, :], bar[0], bar[1],
+                  f"{w.name} dense head {HS[hi]} row {r}")

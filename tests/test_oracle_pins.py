@@ -80,6 +80,28 @@ def test_chunk_width_changes_no_value():
         assert np.array_equal(o, outs[0])
 
 
+def test_row_and_head_restriction_and_fp32_views_change_no_value():
+    """P8: restricting block_scores to some rows and heads, and passing the
+    bf16 values as fp32 arrays instead of fp64, leaves those rows' scores
+    bit-identical (every product is formed in fp64 either way); the other
+    rows and heads stay -inf."""
+    lens = (384, 640)
+    cu = S.cu_from_lengths(lens)
+    q, k, v = S.make_qkv(lens, 4, 2, 128, seed=5, sink=True)
+    qf, kf, vf = (t.to(torch.float64).numpy() for t in (q, k, v))
+    q32, k32 = (t.to(torch.float32).numpy() for t in (q, k))
+    bonus = O.value_bonus(vf, cu, 128, 0.2)
+    full = O.block_scores(qf, kf, bonus, cu, 4, 2, 128, 8, 256, 1.0)
+    rows, heads = [0, 2, 4, 7], [1, 2]
+    part = O.block_scores(q32, k32, bonus, cu, 4, 2, 128, 8, 128, 1.0, heads=heads, rows=rows)
+    for h in range(4):
+        for r in range(full.shape[1]):
+            if h in heads and r in rows:
+                assert np.array_equal(part[h, r], full[h, r])
+            else:
+                assert np.all(np.isneginf(part[h, r]))
+
+
 # ---------------------------------------------------------------- P3 (OAM) -----
 
 def test_value_bonus_hand_example():
