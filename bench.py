@@ -8,11 +8,14 @@ default workload is the 128K-token Qwen3-8B-shaped layer (32 query heads, 8
 KV heads, d = 128) at ~25 % kept block pairs, timed against the library's own
 dense causal attention on the same inputs.
 
-    python bench.py [--steps K] [--warmup W] [--no-sweep] [--no-cpu-baseline]
-    python bench.py --fp8        # 36-layer fp8 varlen schedule instead
+    python bench.py [--steps K] [--warmup W] [--no-sweep] [--no-fp8] [--no-cpu-baseline]
 
 Prints ONE JSON line.  value = effective TFLOP/s = dense-equivalent causal
 attention FLOP (4 d Hq sum_z L_z (L_z + 1) / 2) / Stem end-to-end time.
+Besides the headline layer it reports the density sweep at 64K (linearity
+and skip overhead), the fp8 varlen batch (four packed sequences, 128K
+tokens, per-layer times and the 36-layer alpha schedule) and the CPU
+oracle's rate on a bounded sample.
 """
 from __future__ import annotations
 
@@ -101,7 +104,14 @@ class StageTimer:
 
 
 def cpu_baseline(w, q, k, v, idx, cnt, gpu_flop_dense, budget_s=20.0):
-    """Time the oracle on a bounded sample of the same workload and scale by work."""
+    """Time the oracle on a bounded sample of the same workload and scale by work.
+
+    Each stage gets a share of the budget and samples work units until its
+    share is spent: scoring takes whole 2048-token query chunks of successive
+    query heads, selection takes rows with random fp32 scores of the right
+    length, attention takes (head, query-block) rows with the GPU's lists.
+    Every stage's time is scaled by (total work / sampled work).
+    """
     import numpy as np
     import torch
     import oracle as O
@@ -117,57 +127,70 @@ def cpu_baseline(w, q, k, v, idx, cnt, gpu_flop_dense, budget_s=20.0):
     d = 128
     sc = 1.0 / math.sqrt(d)
     parts = []
-    # --- score: head 0, the first query chunks (causal cost grows with the chunk index)
+    # --- v-norm bonus: KV head 0 (same work for every KV head)
     t0 = time.perf_counter()
-    vf = v[:, 0:1, :].to(torch.float64).numpy()
-    bon = O.value_bonus(vf, [0, L], 128, w.beta)
+    O.value_bonus(v[:, 0:1, :].to(torch.float64).numpy(), [0, L], 128, w.beta)
     t_vn = time.perf_counter() - t0
-    qf = q[:, 0:1, :].to(torch.float64).numpy()
-    kf = k[:, 0:1, :].to(torch.float64).numpy()
-    done_pairs, t_sc, c = 0, 0.0, 0
+    # --- score: chunks of query heads 0, G, 2G, ... (one per KV head), in order
     scale = 1.0 / (math.sqrt(d) * w.stride * w.norm)
-    while t_sc < budget_s * 0.4 and c * w.chunk_size < L:
-        c0, c1 = c * w.chunk_size, min((c + 1) * w.chunk_size, L)
-        t0 = time.perf_counter()
-        A = O.strided_scores(qf[:, 0], kf[:, 0], w.stride, scale, c0 // w.stride, c1 // w.stride)
-        m = 128 // w.stride
-        A.reshape((c1 - c0) // 128, m, A.shape[1] // m, m).max(axis=(1, 3))
-        t_sc += time.perf_counter() - t0
-        I0, I1 = c0 // 128, c1 // 128
-        done_pairs += sum(I + 1 for I in range(I0, I1))
-        c += 1
+    m = 128 // w.stride
+    done_pairs, t_sc, n_chunks, heads_used = 0, 0.0, 0, 0
+    for h in range(0, Hq, G):
+        if t_sc >= budget_s * 0.35:
+            break
+        heads_used += 1
+        qf = q[:, h, :].to(torch.float64).numpy()
+        kf = k[:, h // G, :].to(torch.float64).numpy()
+        for c0 in range(0, L, w.chunk_size):
+            if t_sc >= budget_s * 0.35:
+                break
+            c1 = min(c0 + w.chunk_size, L)
+            t0 = time.perf_counter()
+            A = O.strided_scores(qf, kf, w.stride, scale, c0 // w.stride, c1 // w.stride)
+            A.reshape((c1 - c0) // 128, m, A.shape[1] // m, m).max(axis=(1, 3))
+            t_sc += time.perf_counter() - t0
+            done_pairs += sum(I + 1 for I in range(c0 // 128, c1 // 128))
+            n_chunks += 1
     total_pairs = Hq * nb * (nb + 1) / 2
     est_score = t_sc * total_pairs / done_pairs + t_vn * Hkv
-    parts.append(f"score: head 0, {c} chunk(s) of {w.chunk_size} ({done_pairs} of {int(total_pairs)} "
-                 f"block pairs), v-bonus of 1 of {Hkv} KV heads")
-    # --- schedule: 512 rows of head 0 on the GPU's scores are not needed: any
-    # fp32 scores exercise the same work; use random ones of the right shape.
+    parts.append(f"score: {n_chunks} query chunks of {w.chunk_size} over {heads_used} head(s) "
+                 f"({done_pairs} of {int(total_pairs)} block pairs), v-bonus of 1 of {Hkv} KV heads")
+    # --- schedule: rows from the end of the sequence backwards (the longest rows)
     rng = np.random.default_rng(0)
-    rows = list(range(nb - 256, nb))
-    t0 = time.perf_counter()
-    for I in rows:
+    t_tk, n_rows, done_cand = 0.0, 0, 0
+    I = nb - 1
+    while t_tk < budget_s * 0.15:
         row = rng.standard_normal(I + 1).astype(np.float32)
+        t0 = time.perf_counter()
         kept = O.kept_count(I, nb, w.k_start[0], w.mu, w.alpha, w.n_init, w.n_window)
         O.select_row(row, I, kept, O.forced_blocks(I, w.n_init, w.n_window))
-    t_tk = time.perf_counter() - t0
-    est_topk = t_tk * (Hq * nb) / len(rows)
-    parts.append(f"schedule: {len(rows)} of {Hq * nb} rows")
-    # --- BSA: sampled (head, row) pairs with the GPU's lists, spread over rows,
-    # one oracle call (it allocates full-size outputs once per call)
+        t_tk += time.perf_counter() - t0
+        done_cand += I + 1
+        n_rows += 1
+        I = I - 1 if I > 0 else nb - 1
+    est_topk = t_tk * (Hq * nb * (nb + 1) / 2) / done_cand
+    parts.append(f"schedule: {n_rows} rows ({done_cand} of {int(Hq * nb * (nb + 1) / 2)} candidate blocks)")
+    # --- BSA: (head, row) pairs with the GPU's lists, rows spread over the
+    # sequence, one head per KV group; several rows per oracle call
     idx_c, cnt_c = idx.cpu().numpy(), cnt.cpu().numpy()
-    hs = [0, G, 2 * G, 3 * G]
-    sample_rows = [int(x) for x in np.linspace(nb - 1, 0, 24)]
+    hs = list(range(0, Hq, G))[:4]
     qs = q[:, hs, :].to(torch.float64).numpy()
-    ks = k[:, 0:4, :].to(torch.float64).numpy()
-    vs = v[:, 0:4, :].to(torch.float64).numpy()
+    ks = k[:, [h // G for h in hs], :].to(torch.float64).numpy()
+    vs = v[:, [h // G for h in hs], :].to(torch.float64).numpy()
     li, lc = idx_c[hs], cnt_c[hs]
-    work = [(j, r) for r in sample_rows for j in range(len(hs))]
-    t0 = time.perf_counter()
-    O.block_sparse_attention(qs, ks, vs, li, lc, [0, L], len(hs), 4, sc, rows=work)
-    t_bs = time.perf_counter() - t0
-    done = sum((int(lc[j, r]) - 1) * 16384 + 8256 for j, r in work)
+    order = [int(x) for x in np.random.default_rng(1).permutation(nb)]
+    t_bs, done, n_work, pos = 0.0, 0, 0, 0
+    while t_bs < budget_s * 0.5 and pos < nb:
+        rows = order[pos:pos + 8]
+        pos += 8
+        work = [(j, r) for r in rows for j in range(len(hs))]
+        t0 = time.perf_counter()
+        O.block_sparse_attention(qs, ks, vs, li, lc, [0, L], len(hs), len(hs), sc, rows=work)
+        t_bs += time.perf_counter() - t0
+        done += sum((int(lc[j, r]) - 1) * 16384 + 8256 for j, r in work)
+        n_work += len(work)
     est_bsa = t_bs * bsa_pairs_total[0] / done
-    parts.append(f"bsa: {len(work)} (head, query-block) rows, {done} of {bsa_pairs_total[0]} token pairs")
+    parts.append(f"bsa: {n_work} (head, query-block) rows, {done} of {bsa_pairs_total[0]} token pairs")
     est_total = est_score + est_topk + est_bsa
     return {"value": gpu_flop_dense / est_total / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
@@ -277,10 +300,86 @@ def run_main(args):
 
     if not args.no_sweep:
         res["density_sweep"] = density_sweep(args, torch, stem, S, dev)
+    if not args.no_fp8:
+        res["fp8_varlen"] = fp8_varlen(args, torch, stem, S, dev)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle, bounded sample)")
         res["cpu_baseline"] = cpu_baseline(w, q, k, v, idx, cnt, flop_dense)
     print(json.dumps(res), flush=True)
+
+
+def fp8_varlen(args, torch, stem, S, dev):
+    """The fp8 varlen batch: sequences of 8K, 16K, 32K and 72K tokens packed
+    into 128K, 32 q / 8 kv heads.  Scoring runs on the bf16 tensors, attention
+    on their per-(block, head) e4m3 quantisation (done by the harness, outside
+    the timed region).  Layers 0-4 use alpha 1.0 and layers 5-35 alpha 0.7;
+    both kinds are timed on the inputs of layer 0 (the time depends on the
+    lists, not on the draw), and the 36-layer total is 5 t(1.0) + 31 t(0.7).
+    """
+    w_hi, w_lo = S.fp8_workload(0), S.fp8_workload(5)
+    p = stem.Problem(w_hi.cu_seqlens, w_hi.num_q_heads, w_hi.num_kv_heads)
+    log("[bench] fp8 varlen: generating 4 packed sequences, T=131072")
+    q, k, v = S.make_workload_qkv(w_hi)
+    (q8, qs), (k8, ks), (v8, vs) = (S.quantize_e4m3_per_block(t, w_hi.seqlens) for t in (q, k, v))
+    qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    qa, ka, va = q8.to(dev), k8.to(dev), v8.to(dev)
+    scl = (qs.to(dev), ks.to(dev), vs.to(dev))
+    del q, k, v, q8, k8, v8
+    scores = torch.empty((p.Hq, p.R, p.max_nb), dtype=torch.float32, device=dev)
+    ws = torch.empty(stem.stem_score_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    aws = torch.empty(stem.stem_attn_workspace_bytes(p, stem.STEM_DTYPE_FP8_E4M3), dtype=torch.uint8,
+                      device=dev)
+    out = torch.empty((p.T, p.Hq, 128), dtype=torch.bfloat16, device=dev)
+    flop_dense = dense_flop(w_hi.seqlens, w_hi.num_q_heads)
+    dense_pairs = p.Hq * sum(L * (L + 1) / 2 for L in w_hi.seqlens)
+    layers = {}
+    for tag, w in (("alpha_1.0", w_hi), ("alpha_0.7", w_lo)):
+        kcap = stem.stem_max_kept(p, w.k_start, w.mu, w.alpha, w.n_init, w.n_window)
+        idx = torch.empty((p.Hq, p.R, kcap), dtype=torch.int32, device=dev)
+        cnt = torch.empty((p.Hq, p.R), dtype=torch.int32, device=dev)
+        fns = [lambda: stem.stem_score(p, qd, kd, vd, w.stride, w.chunk_size, w.norm, w.beta, scores, ws),
+               lambda: stem.stem_schedule_topk(p, scores, w.k_start, w.mu, w.alpha, w.n_init, w.n_window,
+                                               kcap, idx, cnt),
+               lambda: stem.stem_bsa_prefill(p, qa, ka, va, idx, cnt, scales=scl, out=out, workspace=aws)]
+        timer = StageTimer(torch, ["score", "schedule", "bsa"])
+        for _ in range(max(1, args.warmup)):
+            timer.run(fns)
+        torch.cuda.synchronize()
+        evs = [timer.run(fns) for _ in range(max(3, args.steps // 2))]
+        torch.cuda.synchronize()
+        for ev in evs:
+            timer.collect(ev)
+        pairs = bsa_pairs(idx, cnt, p)
+        t_layer = timer.mean("score") + timer.mean("schedule") + timer.mean("bsa")
+        layers[tag] = {"ms": t_layer, "stages_ms": {n: timer.mean(n) for n in ("score", "schedule", "bsa")},
+                       "computed_pair_fraction": pairs / dense_pairs,
+                       "bsa_tflops": 4.0 * 128 * pairs / (timer.mean("bsa") * 1e-3) / 1e12,
+                       "effective_tflops": flop_dense / (t_layer * 1e-3) / 1e12}
+        log(f"[bench]   fp8 {tag}: layer {t_layer:.2f} ms (bsa {timer.mean('bsa'):.2f} ms, "
+            f"rho {pairs / dense_pairs:.4f})")
+    dtimer = StageTimer(torch, ["dense"])
+    dfn = [lambda: stem.stem_dense_prefill(p, qa, ka, va, scales=scl, out=out, workspace=aws)]
+    dtimer.run(dfn)
+    torch.cuda.synchronize()
+    devs = [dtimer.run(dfn) for _ in range(3)]
+    torch.cuda.synchronize()
+    for ev in devs:
+        dtimer.collect(ev)
+    t_dense = dtimer.mean("dense")
+    lo = layers["alpha_0.7"]
+    for L_ in layers.values():
+        L_["skip_overhead"] = L_["stages_ms"]["bsa"] / (L_["computed_pair_fraction"] * t_dense) - 1.0
+    total = 5 * layers["alpha_1.0"]["ms"] + 31 * lo["ms"]
+    log(f"[bench]   fp8 dense {t_dense:.2f} ms; 36 layers {total:.1f} ms vs dense {36 * t_dense:.1f} ms")
+    return {"workload": "cfg5: fp8 e4m3 varlen, seqlens 8192/16384/32768/73728 (T=131072), 32q/8kv, "
+                        "d128, per-(128-block, head) scales, k_start 18/35/70/156, mu 0.5, 1 sink + 2 window",
+            "layers": layers, "dense_ms": t_dense,
+            "dense_tflops": flop_dense / (t_dense * 1e-3) / 1e12,
+            "ms_36_layers": total, "dense_ms_36_layers": 36 * t_dense,
+            "speedup_vs_dense_36_layers": 36 * t_dense / total,
+            "roofline": {"bound": "mfma", "kernel": "attn_fp8_kernel<sparse>", "achieved": lo["bsa_tflops"],
+                         "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                         "frac": lo["bsa_tflops"] / PEAK_FP8_TFLOPS}}
 
 
 def density_sweep(args, torch, stem, S, dev):
@@ -342,6 +441,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="cfg3_n128k")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device-to-device copies of MIB MiB (to scale the "

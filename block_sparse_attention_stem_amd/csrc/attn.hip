@@ -177,12 +177,13 @@ struct AttnItem {
   int h, g, r, z, I;
 };
 
-// Rows are walked from the last (longest causal prefix) to the first; the
-// G heads of a KV group share an XCD and the chip walks one KV head at a
-// time (see xcd_item).
+// Items are ordered by KV group, then by row from the last (longest causal
+// prefix) to the first, then by the G query heads of the group; each XCD
+// takes a contiguous eighth of that order (xcd_chunk_item), so its L2 serves
+// neighbouring rows of one KV group, which list mostly the same blocks.
 __device__ __forceinline__ AttnItem decode_attn(const AttnLaunch &a, const SeqTable &t, int rows) {
   const int G = a.Hq / a.Hkv;
-  const int item = xcd_item(blockIdx.x, rows * a.Hq, G);
+  const int item = xcd_chunk_item(blockIdx.x, rows * a.Hq);
   const int slot = item / G, hh = item - slot * G;
   AttnItem w;
   w.g = slot / rows;

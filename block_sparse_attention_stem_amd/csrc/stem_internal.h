@@ -51,7 +51,20 @@ __device__ __forceinline__ int xcd_item(int b, int n_items, int G) {
   return slot * G + (j >> 3);
 }
 
-// Token-Position-Decay budget: k(I) = floor(ke - ke (1 - mu) I / nb), with
+// Work-item order that gives each XCD a contiguous eighth of the items:
+// workgroup b runs on XCD b % 8 as the (b / 8)-th workgroup that XCD
+// receives, so XCD x walks items [x n/8, (x+1) n/8) in order.  With items
+// ordered KV group first, then rows, then the G heads of a row, each XCD
+// (own L2) keeps neighbouring rows of one KV group in flight, and those
+// rows' heads list mostly the same K/V blocks.  A ragged tail (n not a
+// multiple of 8) keeps the identity order.
+__device__ __forceinline__ int xcd_chunk_item(int b, int n_items) {
+  const int per = n_items >> 3;
+  if (b >= per * 8) return b;
+  return (b & 7) * per + (b >> 3);
+}
+
+// Token-Position-Decay budget// Token-Position-Decay budget: k(I) = floor(ke - ke (1 - mu) I / nb), with
 // ke = alpha * k_start already folded in.  Evaluated in fp64 without
 // contraction; the 1e-9 nudge absorbs the rounding of the fp64 steps when the
 // exact (decimal) value is an integer.
