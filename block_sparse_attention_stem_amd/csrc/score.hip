@@ -11,8 +11,10 @@
 //   vstats  bonus = beta * max(0, zscore(l)) per (sequence, KV head)
 //   score   strided anti-diagonal GEMM on bf16 MFMA, with the causal mask,
 //           the 16x16 max-pool, the 1/(sqrt(d) s n) scale and the bonus fused
-//           into the epilogue.  Only the causal triangle of 128x128 strided
+//           into the epilogue.  Only the causal triangle of 256x128 strided
 //           tiles is launched; scores never touch HBM before pooling.
+#include <utility>
+
 #include "stem_internal.h"
 #include "gfx950_util.h"
 
@@ -101,16 +103,26 @@ hipError_t launch_vstats(const ScoreLaunch &a, const SeqTable &t, hipStream_t s)
 }
 
 // ------------------------------------------------------------------ score
-// Workgroup tile: 128 strided query rows x 128 strided key rows (= 8 x 8
+// Workgroup tile: 256 strided query rows x 128 strided key rows (= 16 x 8
 // blocks of 16 strided rows), K = s*d = 1024 walked in 16 chunks of 64.
 // Row i of the A matrix is Q[tok + i*s + t][h][:] for t = 0..s-1; row j of B
 // is K[tok + j*s + (s-1-t)][g][:] (the anti-diagonal pairing).  Chunk c
-// covers t = c / 2 and head dims (c % 2) * 64 .. +63, so every lane's load is
-// 16 contiguous bytes of one token row.
-// Four waves in a 2x2 grid, each 64x64 = 2x2 MFMA 32x32 tiles.
-constexpr int kScoreTile = 128;
-constexpr int kScoreBK = 64;
-constexpr int kLdsRow = kScoreBK + 8;   // 144-byte rows: conflict-free 16 B reads
+// covers t = c / 2 and head dims (c % 2) * 64 .. +63: one 128-byte piece of
+// one token row per matrix row.
+//
+// Eight waves (two per SIMD) in a 4 x 2 grid, each 64 x 64 = 2 x 2 MFMA 32x32
+// tiles.  Chunks arrive by direct-to-LDS buffer loads into a ring of three
+// stages (separate LDS arrays, the chunk loop fully unrolled), requested two
+// chunks ahead: one barrier per chunk, no staging registers.  LDS rows are
+// 128 bytes; a row's 16-byte pieces are stored XOR-permuted by (row / 2) % 8,
+// so the 32 x 16-byte fragment reads of an MFMA hit every bank once.  The
+// permutation is applied on the global side of the loads (each lane fetches
+// the piece that belongs at its fixed LDS slot).
+constexpr int kRowsA = 256;                 // strided query rows per tile
+constexpr int kRowsB = 128;                 // strided key rows per tile
+constexpr int kScoreBK = 64;                // K elements per chunk
+constexpr int kChunks = 8 * kHeadDim / kScoreBK;   // 16
+constexpr uint32_t kScoreBufWord3 = 0x00020000u;   // raw buffer descriptor word 3 (gfx9 dword access)
 
 struct ScoreArgs {
   const __bf16 *q, *k;
@@ -120,60 +132,103 @@ struct ScoreArgs {
   float scale;
 };
 
-__device__ __forceinline__ void tri_decode(int p, int &ti, int &tj) {
-  // p = ti*(ti+1)/2 + tj, 0 <= tj <= ti
-  int r = (int)((sqrtf(8.f * (float)p + 1.f) - 1.f) * 0.5f);
-  while ((r + 1) * (r + 2) / 2 <= p) ++r;
-  while (r * (r + 1) / 2 > p) --r;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Tile pair p of a (sequence, head) -> (row band ti, column band tj); band
+// ti starts at pair ti (ti + 1) (see score_pairs).
+__device__ __forceinline__ void band_decode(int p, int &ti, int &tj) {
+  int r = (int)((sqrtf(4.f * (float)p + 1.f) - 1.f) * 0.5f);
+  while ((r + 1) * (r + 2) <= p) ++r;
+  while (r * (r + 1) > p) --r;
   ti = r;
-  tj = p - r * (r + 1) / 2;
+  tj = p - r * (r + 1);
 }
 
-__global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, SeqTable t, int n_items) {
-  __shared__ __attribute__((aligned(16))) __bf16 As[2][kScoreTile * kLdsRow];
-  __shared__ __attribute__((aligned(16))) __bf16 Bs[2][kScoreTile * kLdsRow];
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt[3:0] | expcnt 7 | lgkmcnt 15 | vmcnt[5:4]).
+template <int N>
+__device__ __forceinline__ void score_wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+// Barrier that waits for this wave's LDS reads but not for its loads in flight.
+__device__ __forceinline__ void score_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int item = xcd_item(blockIdx.x, n_items, a.G);
+template <typename F, int... Is>
+__device__ __forceinline__ void score_static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void score_static_for(F &&f) {
+  score_static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, int n_items) {
+  __shared__ __attribute__((aligned(1024))) uint16_t A0[kRowsA * kScoreBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t A1[kRowsA * kScoreBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t A2[kRowsA * kScoreBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t B0[kRowsB * kScoreBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t B1[kRowsB * kScoreBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t B2[kRowsB * kScoreBK];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int item = xcd_chunk_item(blockIdx.x, n_items);
   const int slot = item / a.G, hh = item - slot * a.G;
-  // slot -> (sequence, KV head, tile pair); item prefix counts slots
+  // slot -> (sequence, KV head, tile); item prefix counts slots
   const int z = seq_of(t.item, t.n, slot);
   const int local = slot - t.item[z];
   const int nb = t.row[z + 1] - t.row[z];
-  const int nt = (nb + 7) >> 3;
-  const int npairs = nt * (nt + 1) / 2;
+  const int npairs = score_pairs(nb);
   const int g = local / npairs;
   const int pair = local - g * npairs;
   const int h = g * a.G + hh;
   int ti, tj;
-  tri_decode(pair, ti, tj);
-
+  band_decode(pair, ti, tj);
   const int n_rows = nb * (kBlock / 8);         // strided rows of this sequence
+  const int ibase = ti * kRowsA, jbase = tj * kRowsB;
   const size_t tok0 = (size_t)t.tok[z];
 
-  // global -> register staging: thread covers rows (tid>>3) + 32p, 16 B col
-  const int lrow = tid >> 3, lcol = tid & 7;
-  u32x4 ra[4], rb[4];
-  auto load_chunk = [&](int c) {
-    const int tt = c >> 1, c0 = (c & 1) * kScoreBK + lcol * 8;
+  // Loads: per chunk 32 instructions for A (2048 16-byte slots) and 16 for
+  // B (1024); wave w issues A instructions w + 8 m (m < 4) and B
+  // instructions w + 8 m (m < 2).  Slot s = 64 k + lane sits at LDS row
+  // s / 8, position s % 8, and holds logical piece (s % 8) ^ ((row / 2) % 8)
+  // of that row.  Rows past the sequence re-read its last row.
+  uint32_t voffA[4], voffB[2];
+  {
+    const uint32_t strideA = (uint32_t)a.Hq * kHeadDim * 2 * 8, strideB = (uint32_t)a.Hkv * kHeadDim * 2 * 8;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      int i = ti * kScoreTile + lrow + 32 * p;
-      int j = tj * kScoreTile + lrow + 32 * p;
-      i = i < n_rows ? i : n_rows - 1;
-      j = j < n_rows ? j : n_rows - 1;
-      const size_t qt = tok0 + (size_t)i * 8 + tt;
-      const size_t kt = tok0 + (size_t)j * 8 + (7 - tt);
-      ra[p] = ld16(a.q + (qt * a.Hq + h) * kHeadDim + c0);
-      rb[p] = ld16(a.k + (kt * a.Hkv + g) * kHeadDim + c0);
+    for (int m = 0; m < 4; ++m) {
+      const int sl = 64 * (wave + 8 * m) + lane, row = sl >> 3, lc = (sl & 7) ^ ((row >> 1) & 7);
+      const int rr = (ibase + row < n_rows ? ibase + row : n_rows - 1) - ibase;
+      voffA[m] = (uint32_t)rr * strideA + 16 * lc;
     }
-  };
-  auto store_chunk = [&](int buf) {
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      st16(&As[buf][(lrow + 32 * p) * kLdsRow + lcol * 8], ra[p]);
-      st16(&Bs[buf][(lrow + 32 * p) * kLdsRow + lcol * 8], rb[p]);
+    for (int m = 0; m < 2; ++m) {
+      const int sl = 64 * (wave + 8 * m) + lane, row = sl >> 3, lc = (sl & 7) ^ ((row >> 1) & 7);
+      const int rr = (jbase + row < n_rows ? jbase + row : n_rows - 1) - jbase;
+      voffB[m] = (uint32_t)rr * strideB + 16 * lc;
     }
+  }
+  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.q + ((tok0 + 8 * (size_t)ibase) * a.Hq + h) * kHeadDim), (short)0, 0x7fffffff, kScoreBufWord3);
+  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(a.k + ((tok0 + 8 * (size_t)jbase) * a.Hkv + g) * kHeadDim), (short)0, 0x7fffffff, kScoreBufWord3);
+  const uint32_t tokA = (uint32_t)a.Hq * kHeadDim * 2, tokB = (uint32_t)a.Hkv * kHeadDim * 2;
+  // chunk c: token t = c / 2 of the stride group (reversed for K), dims 64 (c % 2)
+  auto issue = [&](int c, uint16_t *Ad, uint16_t *Bd) __attribute__((always_inline)) {
+    const int tt = c >> 1, d2 = (c & 1) * kScoreBK * 2;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void_t *)(Ad + (wave + 8 * m) * 512), 16, voffA[m],
+                                               (int)(tt * tokA + d2), 0, 0);
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void_t *)(Bd + (wave + 8 * m) * 512), 16, voffB[m],
+                                               (int)((7 - tt) * tokB + d2), 0, 0);
   };
 
   f32x16 acc[2][2];
@@ -183,43 +238,65 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, SeqTable t, int
     for (int nj = 0; nj < 2; ++nj) acc[mi][nj] = f32x16{};
 
   const int wm = wave >> 1, wn = wave & 1;
-  const int frow = lane & 31, fk = (lane >> 5) * 8;
-  constexpr int kChunks = 8 * kHeadDim / kScoreBK;   // s*d / 64 = 16
+  const int frow = lane & 31, lg = lane >> 5;
+  // fragment rows wm*64 + 32 mi + frow (A) and wn*64 + 32 nj + frow (B): the
+  // permutation key (row / 2) % 8 is (frow / 2) % 8 for all of them
+  const int swz = (frow >> 1) & 7;
+  int poff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) poff[ks] = 8 * ((2 * ks + lg) ^ swz);
+  const int rowA = (wm * 64 + frow) * kScoreBK, rowB = (wn * 64 + frow) * kScoreBK;
 
-  load_chunk(0);
-  store_chunk(0);
-  __syncthreads();
-  for (int c = 0; c < kChunks; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < kChunks) load_chunk(c + 1);
+  auto compute = [&](const uint16_t *As, const uint16_t *Bs) __attribute__((always_inline)) {
+    u32x4 fa[2][2], fb[2][2];
 #pragma unroll
-    for (int ks = 0; ks < kScoreBK / 16; ++ks) {
-      bf16x8 fa[2], fb[2];
+    for (int mi = 0; mi < 2; ++mi) fa[0][mi] = ld16(As + rowA + 32 * mi * kScoreBK + poff[0]);
+#pragma unroll
+    for (int nj = 0; nj < 2; ++nj) fb[0][nj] = ld16(Bs + rowB + 32 * nj * kScoreBK + poff[0]);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks + 1 < 4) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) fa[(ks + 1) & 1][mi] = ld16(As + rowA + 32 * mi * kScoreBK + poff[ks + 1]);
+#pragma unroll
+        for (int nj = 0; nj < 2; ++nj) fb[(ks + 1) & 1][nj] = ld16(Bs + rowB + 32 * nj * kScoreBK + poff[ks + 1]);
+      }
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
-        fa[mi] = as_bf16x8(ld16(&As[buf][(wm * 64 + mi * 32 + frow) * kLdsRow + ks * 16 + fk]));
 #pragma unroll
-      for (int nj = 0; nj < 2; ++nj)
-        fb[nj] = as_bf16x8(ld16(&Bs[buf][(wn * 64 + nj * 32 + frow) * kLdsRow + ks * 16 + fk]));
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int nj = 0; nj < 2; ++nj) acc[mi][nj] = mfma_bf16_32x32x16(fa[mi], fb[nj], acc[mi][nj]);
+        for (int nj = 0; nj < 2; ++nj)
+          acc[mi][nj] = mfma_bf16_32x32x16(as_bf16x8(fa[ks & 1][mi]), as_bf16x8(fb[ks & 1][nj]), acc[mi][nj]);
     }
-    if (c + 1 < kChunks) store_chunk(buf ^ 1);
-    __syncthreads();
-  }
+  };
+
+  issue(0, A0, B0);
+  issue(1, A1, B1);
+  score_static_for<kChunks>([&](auto C_) {
+    constexpr int c = decltype(C_)::value;
+    if constexpr (c + 1 < kChunks) score_wait_vmcnt<6>();   // chunk c+1's six loads may still fly
+    else score_wait_vmcnt<0>();
+    score_sync();                                          // chunk c everywhere; stage of c-1 free
+    if constexpr (c + 2 < kChunks) {
+      if constexpr ((c + 2) % 3 == 0) issue(c + 2, A0, B0);
+      else if constexpr ((c + 2) % 3 == 1) issue(c + 2, A1, B1);
+      else issue(c + 2, A2, B2);
+    }
+    __builtin_amdgcn_sched_barrier(0);                     // keep the loads ahead of this chunk's MFMAs
+    if constexpr (c % 3 == 0) compute(A0, B0);
+    else if constexpr (c % 3 == 1) compute(A1, B1);
+    else compute(A2, B2);
+  });
 
   // ---- epilogue: causal mask, 16x16 max-pool, scale, bonus
-  const bool diag = (ti == tj);
+  const bool diag = tj >= 2 * ti;              // some key column of the tile lies past some query row
   const size_t srow0 = ((size_t)h * a.R + t.row[z]) * a.max_nb;
   const float *bon = a.bonus + (size_t)g * a.R + t.row[z];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
     for (int nj = 0; nj < 2; ++nj) {
-      const int ib = ti * kScoreTile + wm * 64 + mi * 32;   // strided row base
-      const int jb = tj * kScoreTile + wn * 64 + nj * 32;
+      const int ib = ibase + wm * 64 + mi * 32;   // strided row base
+      const int jb = jbase + wn * 64 + nj * 32;
       const int j = jb + (lane & 31);
       float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
@@ -246,14 +323,16 @@ __global__ __launch_bounds__(256) void score_kernel(ScoreArgs a, SeqTable t, int
       }
     }
   }
-  if (diag) {
-    // -inf for the columns this row band never computes: J beyond the tile
-    // (non-causal) and J >= nb (past the sequence, up to max_nb).
-    int jstart = (ti + 1) * 8;
+  const int nt_c = (nb + 7) / 8;
+  const int tj_last = 2 * ti + 1 < nt_c - 1 ? 2 * ti + 1 : nt_c - 1;
+  if (tj == tj_last) {
+    // -inf for the columns this row band never computes: J past its last
+    // column band (non-causal) and J >= nb (past the sequence, up to max_nb).
+    int jstart = (tj_last + 1) * 8;
     if (jstart > nb) jstart = nb;
     const int width = a.max_nb - jstart;
-    for (int e = tid; e < 8 * width; e += 256) {
-      const int I = ti * 8 + e / width, J = jstart + e % width;
+    for (int e = tid; e < 16 * width; e += 512) {
+      const int I = ti * 16 + e / width, J = jstart + e % width;
       if (I < nb) a.scores[srow0 + (size_t)I * a.max_nb + J] = -INFINITY;
     }
   }
@@ -271,7 +350,7 @@ hipError_t launch_score(const ScoreLaunch &l, const SeqTable &t, int n_items, hi
   a.max_nb = l.max_nb;
   a.G = l.Hq / l.Hkv;
   a.scale = l.scale;
-  hipLaunchKernelGGL(score_kernel, dim3(n_items), dim3(256), 0, s, a, t, n_items);
+  hipLaunchKernelGGL(score_kernel, dim3(n_items), dim3(512), 0, s, a, t, n_items);
   return hipGetLastError();
 }
 

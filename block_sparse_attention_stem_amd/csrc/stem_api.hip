@@ -113,10 +113,10 @@ int stem_score(const stem_problem_t *p, const void *q, const void *k, const void
     fill_table(p, z0, n, &t);
     if (launch_vstats(a, t, hs) != hipSuccess) return STEM_ERR_HIP;
   }
-  // Score tiles: per sequence, Hkv x (tile pairs of the causal triangle)
-  // slots, each run for the G query heads of the group.  Query rows are
-  // visited chunk_size tokens at a time within a slot order that is
-  // tile-row major, so chunk_size only orders the work.
+  // Score tiles: per sequence, Hkv x (tiles of the causal triangle) slots,
+  // each run for the G query heads of the group.  chunk_size only names the
+  // query-axis tiling of the pages; it changes no value and the kernel's
+  // own tiles replace it.
   const int G = s.Hq / s.Hkv;
   for (int z0 = 0; z0 < s.B; z0 += kMaxSeqsPerLaunch) {
     const int n = s.B - z0 < kMaxSeqsPerLaunch ? s.B - z0 : kMaxSeqsPerLaunch;
@@ -126,8 +126,7 @@ int stem_score(const stem_problem_t *p, const void *q, const void *k, const void
     for (int i = 0; i < n; ++i) {
       t.item[i] = (int32_t)slots;
       const int nb = t.row[i + 1] - t.row[i];
-      const int nt = (nb + 7) / 8;
-      slots += (int64_t)s.Hkv * nt * (nt + 1) / 2;
+      slots += (int64_t)s.Hkv * score_pairs(nb);
     }
     t.item[n] = (int32_t)slots;
     const int64_t items = slots * G;
