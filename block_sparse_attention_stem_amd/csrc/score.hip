@@ -11,7 +11,7 @@
 //   vstats  bonus = beta * max(0, zscore(l)) per (sequence, KV head)
 //   score   strided anti-diagonal GEMM on bf16 MFMA, with the causal mask,
 //           the 16x16 max-pool, the 1/(sqrt(d) s n) scale and the bonus fused
-//           into the epilogue.  Only the causal triangle of 256x128 strided
+//           into the epilogue.  Only the causal triangle of 256x256 strided
 //           tiles is launched; scores never touch HBM before pooling.
 #include <utility>
 
@@ -103,25 +103,28 @@ hipError_t launch_vstats(const ScoreLaunch &a, const SeqTable &t, hipStream_t s)
 }
 
 // ------------------------------------------------------------------ score
-// Workgroup tile: 256 strided query rows x 128 strided key rows (= 16 x 8
-// blocks of 16 strided rows), K = s*d = 1024 walked in 16 chunks of 64.
+// Workgroup tile: 256 strided query rows x 256 strided key rows (= 16 x 16
+// blocks of 16 strided rows), K = s*d = 1024 walked in 32 chunks of 32.
 // Row i of the A matrix is Q[tok + i*s + t][h][:] for t = 0..s-1; row j of B
 // is K[tok + j*s + (s-1-t)][g][:] (the anti-diagonal pairing).  Chunk c
-// covers t = c / 2 and head dims (c % 2) * 64 .. +63: one 128-byte piece of
+// covers t = c / 4 and head dims (c % 4) * 32 .. +31: one 64-byte piece of
 // one token row per matrix row.
 //
-// Eight waves (two per SIMD) in a 4 x 2 grid, each 64 x 64 = 2 x 2 MFMA 32x32
-// tiles.  Chunks arrive by direct-to-LDS buffer loads into a ring of three
-// stages (separate LDS arrays, the chunk loop fully unrolled), requested two
-// chunks ahead: one barrier per chunk, no staging registers.  LDS rows are
-// 128 bytes; a row's 16-byte pieces are stored XOR-permuted by (row / 2) % 8,
-// so the 32 x 16-byte fragment reads of an MFMA hit every bank once.  The
+// Eight waves (two per SIMD) in a 4 x 2 grid, each 64 x 128 = 2 x 4 MFMA
+// 32x32 tiles: a fragment read from LDS feeds two (A) or four (B) MFMAs
+// (768 LDS bytes per MFMA).  Chunks arrive by direct-to-LDS buffer loads
+// into a ring of four stages (separate LDS arrays, the chunk loop fully
+// unrolled), requested four chunks ahead, with one barrier per chunk and no
+// staging registers; a chunk's fragments are read into registers while the
+// previous chunk's MFMAs run, so LDS latency is never waited on.  LDS rows
+// are 64 bytes; a row's 16-byte pieces are stored XOR-permuted by (row / 4)
+// % 4, so the fragment reads of an MFMA hit every bank once.  The
 // permutation is applied on the global side of the loads (each lane fetches
 // the piece that belongs at its fixed LDS slot).
-constexpr int kRowsA = 256;                 // strided query rows per tile
-constexpr int kRowsB = 128;                 // strided key rows per tile
-constexpr int kScoreBK = 64;                // K elements per chunk
-constexpr int kChunks = 8 * kHeadDim / kScoreBK;   // 16
+constexpr int kTileS = 256;                 // strided rows per tile side
+constexpr int kScoreBK = 32;                // K elements per chunk
+constexpr int kChunks = 8 * kHeadDim / kScoreBK;   // 32
+constexpr int kStages = 4;
 constexpr uint32_t kScoreBufWord3 = 0x00020000u;   // raw buffer descriptor word 3 (gfx9 dword access)
 
 struct ScoreArgs {
@@ -134,14 +137,14 @@ struct ScoreArgs {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-// Tile pair p of a (sequence, head) -> (row band ti, column band tj); band
-// ti starts at pair ti (ti + 1) (see score_pairs).
-__device__ __forceinline__ void band_decode(int p, int &ti, int &tj) {
-  int r = (int)((sqrtf(4.f * (float)p + 1.f) - 1.f) * 0.5f);
-  while ((r + 1) * (r + 2) <= p) ++r;
-  while (r * (r + 1) > p) --r;
+// Tile pair p of a (sequence, head) -> (row band ti, column band tj <= ti),
+// p = ti (ti + 1) / 2 + tj.
+__device__ __forceinline__ void tri_decode(int p, int &ti, int &tj) {
+  int r = (int)((sqrtf(8.f * (float)p + 1.f) - 1.f) * 0.5f);
+  while ((r + 1) * (r + 2) / 2 <= p) ++r;
+  while (r * (r + 1) / 2 > p) --r;
   ti = r;
-  tj = p - r * (r + 1);
+  tj = p - r * (r + 1) / 2;
 }
 
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt[3:0] | expcnt 7 | lgkmcnt 15 | vmcnt[5:4]).
@@ -167,12 +170,14 @@ __device__ __forceinline__ void score_static_for(F &&f) {
 }
 
 __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, int n_items) {
-  __shared__ __attribute__((aligned(1024))) uint16_t A0[kRowsA * kScoreBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t A1[kRowsA * kScoreBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t A2[kRowsA * kScoreBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t B0[kRowsB * kScoreBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t B1[kRowsB * kScoreBK];
-  __shared__ __attribute__((aligned(1024))) uint16_t B2[kRowsB * kScoreBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t A0[kTileS * kScoreBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t A1[kTileS * kScoreBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t A2[kTileS * kScoreBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t A3[kTileS * kScoreBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t B0[kTileS * kScoreBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t B1[kTileS * kScoreBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t B2[kTileS * kScoreBK];
+  __shared__ __attribute__((aligned(1024))) uint16_t B3[kTileS * kScoreBK];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -187,30 +192,26 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
   const int pair = local - g * npairs;
   const int h = g * a.G + hh;
   int ti, tj;
-  band_decode(pair, ti, tj);
+  tri_decode(pair, ti, tj);
   const int n_rows = nb * (kBlock / 8);         // strided rows of this sequence
-  const int ibase = ti * kRowsA, jbase = tj * kRowsB;
+  const int ibase = ti * kTileS, jbase = tj * kTileS;
   const size_t tok0 = (size_t)t.tok[z];
 
-  // Loads: per chunk 32 instructions for A (2048 16-byte slots) and 16 for
-  // B (1024); wave w issues A instructions w + 8 m (m < 4) and B
-  // instructions w + 8 m (m < 2).  Slot s = 64 k + lane sits at LDS row
-  // s / 8, position s % 8, and holds logical piece (s % 8) ^ ((row / 2) % 8)
-  // of that row.  Rows past the sequence re-read its last row.
-  uint32_t voffA[4], voffB[2];
+  // Loads: per chunk 16 instructions for A (1024 16-byte slots) and 16 for
+  // B; wave w issues A and B instructions w + 8 m (m < 2).  Slot s = 64 k +
+  // lane sits at LDS row s / 4, position s % 4, and holds logical piece
+  // (s % 4) ^ ((row / 4) % 4) of that row.  Rows past the sequence re-read
+  // its last row.
+  uint32_t voffA[2], voffB[2];
   {
     const uint32_t strideA = (uint32_t)a.Hq * kHeadDim * 2 * 8, strideB = (uint32_t)a.Hkv * kHeadDim * 2 * 8;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int sl = 64 * (wave + 8 * m) + lane, row = sl >> 3, lc = (sl & 7) ^ ((row >> 1) & 7);
-      const int rr = (ibase + row < n_rows ? ibase + row : n_rows - 1) - ibase;
-      voffA[m] = (uint32_t)rr * strideA + 16 * lc;
-    }
-#pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const int sl = 64 * (wave + 8 * m) + lane, row = sl >> 3, lc = (sl & 7) ^ ((row >> 1) & 7);
-      const int rr = (jbase + row < n_rows ? jbase + row : n_rows - 1) - jbase;
-      voffB[m] = (uint32_t)rr * strideB + 16 * lc;
+      const int sl = 64 * (wave + 8 * m) + lane, row = sl >> 2, lc = (sl & 3) ^ ((row >> 2) & 3);
+      const int ra = (ibase + row < n_rows ? ibase + row : n_rows - 1) - ibase;
+      const int rb = (jbase + row < n_rows ? jbase + row : n_rows - 1) - jbase;
+      voffA[m] = (uint32_t)ra * strideA + 16 * lc;
+      voffB[m] = (uint32_t)rb * strideB + 16 * lc;
     }
   }
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
@@ -218,85 +219,105 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
   const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(a.k + ((tok0 + 8 * (size_t)jbase) * a.Hkv + g) * kHeadDim), (short)0, 0x7fffffff, kScoreBufWord3);
   const uint32_t tokA = (uint32_t)a.Hq * kHeadDim * 2, tokB = (uint32_t)a.Hkv * kHeadDim * 2;
-  // chunk c: token t = c / 2 of the stride group (reversed for K), dims 64 (c % 2)
+  // chunk c: token t = c / 4 of the stride group (reversed for K), dims 32 (c % 4)
   auto issue = [&](int c, uint16_t *Ad, uint16_t *Bd) __attribute__((always_inline)) {
-    const int tt = c >> 1, d2 = (c & 1) * kScoreBK * 2;
+    const int tt = c >> 2, d2 = (c & 3) * kScoreBK * 2;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 2; ++m) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void_t *)(Ad + (wave + 8 * m) * 512), 16, voffA[m],
                                                (int)(tt * tokA + d2), 0, 0);
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void_t *)(Bd + (wave + 8 * m) * 512), 16, voffB[m],
                                                (int)((7 - tt) * tokB + d2), 0, 0);
+    }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[2][4];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-    for (int nj = 0; nj < 2; ++nj) acc[mi][nj] = f32x16{};
+    for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = f32x16{};
 
   const int wm = wave >> 1, wn = wave & 1;
   const int frow = lane & 31, lg = lane >> 5;
-  // fragment rows wm*64 + 32 mi + frow (A) and wn*64 + 32 nj + frow (B): the
-  // permutation key (row / 2) % 8 is (frow / 2) % 8 for all of them
-  const int swz = (frow >> 1) & 7;
-  int poff[4];
+  // fragment rows wm*64 + 32 mi + frow (A) and wn*128 + 32 nj + frow (B):
+  // the permutation key (row / 4) % 4 is (frow / 4) % 4 for all of them
+  const int swz = (frow >> 2) & 3;
+  int poff[2];
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) poff[ks] = 8 * ((2 * ks + lg) ^ swz);
-  const int rowA = (wm * 64 + frow) * kScoreBK, rowB = (wn * 64 + frow) * kScoreBK;
+  for (int ks = 0; ks < 2; ++ks) poff[ks] = 8 * ((2 * ks + lg) ^ swz);
+  const int rowA = (wm * 64 + frow) * kScoreBK, rowB = (wn * 128 + frow) * kScoreBK;
 
-  auto compute = [&](const uint16_t *As, const uint16_t *Bs) __attribute__((always_inline)) {
-    u32x4 fa[2][2], fb[2][2];
+  // Fragments of a chunk: 2 k-steps x (2 A + 4 B) 16-byte reads.
+  typedef u32x4 Frags[2][6];
+  auto read_frags = [&](Frags &f, const uint16_t *As, const uint16_t *Bs) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mi = 0; mi < 2; ++mi) fa[0][mi] = ld16(As + rowA + 32 * mi * kScoreBK + poff[0]);
+    for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
-    for (int nj = 0; nj < 2; ++nj) fb[0][nj] = ld16(Bs + rowB + 32 * nj * kScoreBK + poff[0]);
+      for (int mi = 0; mi < 2; ++mi) f[ks][mi] = ld16(As + rowA + 32 * mi * kScoreBK + poff[ks]);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks + 1 < 4) {
+      for (int nj = 0; nj < 4; ++nj) f[ks][2 + nj] = ld16(Bs + rowB + 32 * nj * kScoreBK + poff[ks]);
+    }
+  };
+  auto mfmas = [&](const Frags &f) __attribute__((always_inline)) {
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi) fa[(ks + 1) & 1][mi] = ld16(As + rowA + 32 * mi * kScoreBK + poff[ks + 1]);
-#pragma unroll
-        for (int nj = 0; nj < 2; ++nj) fb[(ks + 1) & 1][nj] = ld16(Bs + rowB + 32 * nj * kScoreBK + poff[ks + 1]);
-      }
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int nj = 0; nj < 2; ++nj)
-          acc[mi][nj] = mfma_bf16_32x32x16(as_bf16x8(fa[ks & 1][mi]), as_bf16x8(fb[ks & 1][nj]), acc[mi][nj]);
-    }
+        for (int nj = 0; nj < 4; ++nj)
+          acc[mi][nj] = mfma_bf16_32x32x16(as_bf16x8(f[ks][mi]), as_bf16x8(f[ks][2 + nj]), acc[mi][nj]);
+  };
+  auto stage_issue = [&](auto S_, int c) __attribute__((always_inline)) {
+    constexpr int st = decltype(S_)::value;
+    if constexpr (st == 0) issue(c, A0, B0);
+    else if constexpr (st == 1) issue(c, A1, B1);
+    else if constexpr (st == 2) issue(c, A2, B2);
+    else issue(c, A3, B3);
+  };
+  auto stage_read = [&](auto S_, Frags &f) __attribute__((always_inline)) {
+    constexpr int st = decltype(S_)::value;
+    if constexpr (st == 0) read_frags(f, A0, B0);
+    else if constexpr (st == 1) read_frags(f, A1, B1);
+    else if constexpr (st == 2) read_frags(f, A2, B2);
+    else read_frags(f, A3, B3);
   };
 
-  issue(0, A0, B0);
-  issue(1, A1, B1);
+  // Step c: wait for chunk c+1, barrier (chunk c's fragments, read in step
+  // c-1, are out of its stage everywhere), load chunk c+4 into that stage,
+  // read chunk c+1's fragments, run chunk c's MFMAs from registers.
+  Frags fr[2];
+  score_static_for<kStages>([&](auto C_) {
+    stage_issue(std::integral_constant<int, decltype(C_)::value>{}, decltype(C_)::value);
+  });
+  score_wait_vmcnt<4 * (kStages - 1)>();
+  score_sync();
+  stage_read(std::integral_constant<int, 0>{}, fr[0]);
   score_static_for<kChunks>([&](auto C_) {
     constexpr int c = decltype(C_)::value;
-    if constexpr (c + 1 < kChunks) score_wait_vmcnt<6>();   // chunk c+1's six loads may still fly
-    else score_wait_vmcnt<0>();
-    score_sync();                                          // chunk c everywhere; stage of c-1 free
-    if constexpr (c + 2 < kChunks) {
-      if constexpr ((c + 2) % 3 == 0) issue(c + 2, A0, B0);
-      else if constexpr ((c + 2) % 3 == 1) issue(c + 2, A1, B1);
-      else issue(c + 2, A2, B2);
+    if constexpr (c + 1 < kChunks) {
+      // loads of chunks c+2 .. c+3 (4 per wave each) may still fly
+      constexpr int later = (kChunks - 2 - c < kStages - 2 ? kChunks - 2 - c : kStages - 2) * 4;
+      score_wait_vmcnt<later>();
+      score_sync();
+      if constexpr (c + kStages < kChunks)
+        stage_issue(std::integral_constant<int, c % kStages>{}, c + kStages);
+      stage_read(std::integral_constant<int, (c + 1) % kStages>{}, fr[(c + 1) & 1]);
     }
-    __builtin_amdgcn_sched_barrier(0);                     // keep the loads ahead of this chunk's MFMAs
-    if constexpr (c % 3 == 0) compute(A0, B0);
-    else if constexpr (c % 3 == 1) compute(A1, B1);
-    else compute(A2, B2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfmas(fr[c & 1]);
+    __builtin_amdgcn_sched_barrier(0);
   });
 
   // ---- epilogue: causal mask, 16x16 max-pool, scale, bonus
-  const bool diag = tj >= 2 * ti;              // some key column of the tile lies past some query row
+  const bool diag = (ti == tj);
   const size_t srow0 = ((size_t)h * a.R + t.row[z]) * a.max_nb;
   const float *bon = a.bonus + (size_t)g * a.R + t.row[z];
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
-    for (int nj = 0; nj < 2; ++nj) {
-      const int ib = ibase + wm * 64 + mi * 32;   // strided row base
-      const int jb = jbase + wn * 64 + nj * 32;
+    for (int nj = 0; nj < 4; ++nj) {
+      const int ib = ibase + wm * 64 + mi * 32;    // strided row base
+      const int jb = jbase + wn * 128 + nj * 32;
       const int j = jb + (lane & 31);
       float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
@@ -323,12 +344,10 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
       }
     }
   }
-  const int nt_c = (nb + 7) / 8;
-  const int tj_last = 2 * ti + 1 < nt_c - 1 ? 2 * ti + 1 : nt_c - 1;
-  if (tj == tj_last) {
-    // -inf for the columns this row band never computes: J past its last
-    // column band (non-causal) and J >= nb (past the sequence, up to max_nb).
-    int jstart = (tj_last + 1) * 8;
+  if (diag) {
+    // -inf for the columns this row band never computes: J beyond the tile
+    // (non-causal) and J >= nb (past the sequence, up to max_nb).
+    int jstart = (ti + 1) * 16;
     if (jstart > nb) jstart = nb;
     const int width = a.max_nb - jstart;
     for (int e = tid; e < 16 * width; e += 512) {

@@ -94,14 +94,11 @@ __host__ __device__ inline int kept_count(int I, int nb, double ke, double mu,
   return k < I + 1 ? k : I + 1;
 }
 
-// Score tiles of one (sequence, query head) with nb blocks: row band ti (256
-// strided rows = 16 blocks) meets column bands tj (128 strided rows = 8
-// blocks) for tj = 0 .. min(2 ti + 1, nt_c - 1); every row band but the last
-// has 2 ti + 2 of them.
+// Score tiles of one (sequence, query head) with nb blocks: the causal
+// triangle of 256 x 256 strided tiles (16 x 16 blocks each).
 __host__ __device__ inline int score_pairs(int nb) {
-  const int nt_r = (nb + 15) / 16, nt_c = (nb + 7) / 8;
-  const int last = 2 * nt_r < nt_c ? 2 * nt_r : nt_c;
-  return (nt_r - 1) * nt_r + last;
+  const int nt = (nb + 15) / 16;
+  return nt * (nt + 1) / 2;
 }
 
 // ---------------------------------------------------------------- launchers
