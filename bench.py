@@ -382,6 +382,85 @@ def fp8_varlen(args, torch, stem, S, dev):
                          "frac": lo["bsa_tflops"] / PEAK_FP8_TFLOPS}}
 
 
+def kstart_for_density(stem, nb, target, alpha=0.7, mu=0.5, n_init=1, n_window=2):
+    """Smallest-error integer k_start for a kept block-pair fraction (library TPD rule)."""
+    total = nb * (nb + 1) / 2
+    best, best_err = 1, 1e9
+    lo, hi = 1, nb
+    while lo <= hi:                  # kept fraction is non-decreasing in k_start
+        mid = (lo + hi) // 2
+        kept = sum(stem.stem_kept_count(I, nb, mid, mu, alpha, n_init, n_window) for I in range(nb))
+        frac = kept / total
+        if abs(frac - target) < best_err or (abs(frac - target) == best_err and mid < best):
+            best, best_err = mid, abs(frac - target)
+        if frac < target:
+            lo = mid + 1
+        else:
+            hi = mid - 1
+    for k in (best - 1, best + 1):
+        if 1 <= k <= nb:
+            kept = sum(stem.stem_kept_count(I, nb, k, mu, alpha, n_init, n_window) for I in range(nb))
+            err = abs(kept / total - target)
+            if err < best_err or (err == best_err and k < best):
+                best, best_err = k, err
+    return best
+
+
+def length_sweep(args, torch, stem, S, dev):
+    """One layer (32 q / 8 kv heads, d 128) at 4K .. 256K tokens, ~25 % kept
+    (alpha 0.7, mu 0.5, 1 sink + 2 window, k_start chosen per length with the
+    library's TPD rule): Stem (score + schedule + BSA) vs the dense kernel."""
+    pts = []
+    for L in (4096, 8192, 16384, 32768, 65536, 131072, 262144):
+        nb = L // 128
+        ks = kstart_for_density(stem, nb, 0.25)
+        log(f"[bench] length sweep: N={L}, k_start {ks}")
+        q, k, v = S.make_qkv((L,), 32, 8, 128, seed=0, sink=True)
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+        del q, k, v
+        p = stem.Problem([0, L], 32, 8)
+        scores = torch.empty((p.Hq, p.R, p.max_nb), dtype=torch.float32, device=dev)
+        ws = torch.empty(stem.stem_score_workspace_bytes(p), dtype=torch.uint8, device=dev)
+        kcap = stem.stem_max_kept(p, [ks], 0.5, 0.7, 1, 2)
+        idx = torch.empty((p.Hq, p.R, kcap), dtype=torch.int32, device=dev)
+        cnt = torch.empty((p.Hq, p.R), dtype=torch.int32, device=dev)
+        out = torch.empty((p.T, p.Hq, 128), dtype=torch.bfloat16, device=dev)
+        aws = torch.empty(stem.stem_attn_workspace_bytes(p, stem.STEM_DTYPE_BF16), dtype=torch.uint8, device=dev)
+        fns = [lambda: stem.stem_score(p, qd, kd, vd, 8, 2048, 1.0, 0.2, scores, ws),
+               lambda: stem.stem_schedule_topk(p, scores, [ks], 0.5, 0.7, 1, 2, kcap, idx, cnt),
+               lambda: stem.stem_bsa_prefill(p, qd, kd, vd, idx, cnt, out=out, workspace=aws)]
+        timer = StageTimer(torch, ["score", "schedule", "bsa"])
+        reps = 3 if L >= 131072 else 8
+        for _ in range(2):
+            timer.run(fns)
+        torch.cuda.synchronize()
+        evs = [timer.run(fns) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for ev in evs:
+            timer.collect(ev)
+        dt = StageTimer(torch, ["dense"])
+        dfn = [lambda: stem.stem_dense_prefill(p, qd, kd, vd, out=out, workspace=aws)]
+        dt.run(dfn)
+        torch.cuda.synchronize()
+        devs = [dt.run(dfn) for _ in range(reps)]
+        torch.cuda.synchronize()
+        for ev in devs:
+            dt.collect(ev)
+        t_stem = timer.mean("score") + timer.mean("schedule") + timer.mean("bsa")
+        t_dense = dt.mean("dense")
+        rho = bsa_pairs(idx, cnt, p) / (p.Hq * L * (L + 1) / 2)
+        pts.append({"seq_len": L, "k_start": ks, "computed_pair_fraction": rho,
+                    "stem_ms": t_stem, "score_ms": timer.mean("score"), "schedule_ms": timer.mean("schedule"),
+                    "bsa_ms": timer.mean("bsa"), "dense_ms": t_dense, "speedup": t_dense / t_stem,
+                    "effective_tflops": dense_flop([L], 32) / (t_stem * 1e-3) / 1e12})
+        log(f"[bench]   N={L}: stem {t_stem:.3f} ms (score {timer.mean('score'):.3f}) dense {t_dense:.3f} ms "
+            f"-> {t_dense / t_stem:.2f}x")
+        del qd, kd, vd, scores, ws, idx, cnt, out, aws
+        torch.cuda.empty_cache()
+    return {"workload": "one layer, 32q/8kv, d128, ~25% kept (alpha 0.7, mu 0.5, 1 sink + 2 window)",
+            "points": pts}
+
+
 def density_sweep(args, torch, stem, S, dev):
     """Config 4: N = 65536, keep 100/50/25/20/10 %: BSA time vs computed fraction."""
     w0 = S.sweep_workload(1.0)
@@ -442,6 +521,8 @@ def main():
     ap.add_argument("--workload", default="cfg3_n128k")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--length-sweep", action="store_true",
+                    help="only run the 4K..256K length sweep (Stem vs dense) and print its JSON")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device-to-device copies of MIB MiB (to scale the "
@@ -461,6 +542,12 @@ def main():
         print("bench.py measures one GPU only: the Stem path here runs on a single MI355X "
               "(no sharding or collectives); run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.length_sweep:
+        import torch
+        import block_sparse_attention_stem_amd as stem
+        import stem_synth as S
+        print(json.dumps({"length_sweep": length_sweep(args, torch, stem, S, torch.device("cuda:0"))}), flush=True)
+        return
     run_main(args)
 
 
