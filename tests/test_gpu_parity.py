@@ -235,3 +235,71 @@ def test_fp8_full_lists_equal_dense(fp8_small):
                               torch.from_numpy(fc).to(dev()), SCALE, scales=sc)
     b = stem.stem_dense_prefill(p, *to_dev(q8, k8, v8), SCALE, scales=sc)
     assert torch.equal(a, b)
+
+
+# ------------------------------------------------------- head-group shapes ----
+
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 1)])
+def test_head_group_ratios(Hq, Hkv):
+    """Multi-head (1 query head per KV head) and 8 query heads on one KV head:
+    scores, lists and attention through the whole path."""
+    lens = (640, 1408)
+    cu = S.cu_from_lengths(lens)
+    q, k, v = make_inputs(lens, Hq, Hkv, seed=11)
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    note(f"[heads] Hq={Hq} Hkv={Hkv} lens={lens}")
+    p = stem.Problem(cu, Hq, Hkv)
+    qd, kd, vd = to_dev(q, k, v)
+    s = stem.stem_score(p, qd, kd, vd)
+    ref = _oracle_scores(qf, kf, vf, cu, Hq, Hkv)
+    check_scores(s.cpu().numpy(), ref, f"Hq={Hq} Hkv={Hkv}")
+    ks = [2, 4]
+    idx, cnt = stem.stem_schedule_topk(p, s, ks, 0.5, 0.7, 1, 2)
+    ri, rc = O.schedule_topk(s.cpu().numpy(), cu, ks, 0.5, 0.7, 1, 2, idx.shape[2])
+    lists_equal(idx.cpu().numpy(), cnt.cpu().numpy(), ri, rc, f"Hq={Hq} Hkv={Hkv}")
+    out, lse = stem.stem_bsa_prefill(p, qd, kd, vd, idx, cnt, SCALE, want_lse=True)
+    ro, rl = O.block_sparse_attention(qf, kf, vf, ri, rc, cu, Hq, Hkv, SCALE)
+    check_out(f64(out), ro, BF16_MAX_ABS, BF16_MEAN_REL, f"bsa Hq={Hq} Hkv={Hkv}")
+    check_lse(lse.cpu().numpy().astype(np.float64), rl, f"bsa Hq={Hq} Hkv={Hkv}")
+    dout = stem.stem_dense_prefill(p, qd, kd, vd, SCALE)
+    do, _ = O.dense_causal_attention(qf, kf, vf, cu, Hq, Hkv, SCALE)
+    check_out(f64(dout), do, BF16_MAX_ABS, BF16_MEAN_REL, f"dense Hq={Hq} Hkv={Hkv}")
+
+
+def test_score_parameters_beta_zero_and_norm():
+    """beta = 0 (no value bonus: the plain strided routing score) and an extra
+    normaliser n = 2 reach the scores exactly as the oracle defines them."""
+    lens = (1024, 896)
+    cu = S.cu_from_lengths(lens)
+    q, k, v = make_inputs(lens, 4, 2, seed=12)
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    p = stem.Problem(cu, 4, 2)
+    qd, kd, vd = to_dev(q, k, v)
+    for beta, norm in [(0.0, 1.0), (0.2, 2.0), (0.5, 0.5)]:
+        s = stem.stem_score(p, qd, kd, vd, 8, 2048, norm, beta)
+        bonus = O.value_bonus(vf, cu, 128, beta)
+        ref = O.block_scores(qf, kf, bonus, cu, 4, 2, 128, 8, 2048, norm)
+        check_scores(s.cpu().numpy(), ref, f"beta={beta} norm={norm}")
+
+
+def test_lists_with_spare_capacity_are_padded():
+    """A list row stride far above the largest kept count: every entry past
+    the count is -1 and attention reads only the counted prefix."""
+    lens = (1536,)
+    cu = S.cu_from_lengths(lens)
+    q, k, v = make_inputs(lens, 2, 1, seed=13)
+    qf, kf, vf = f64(q), f64(k), f64(v)
+    p = stem.Problem(cu, 2, 1)
+    qd, kd, vd = to_dev(q, k, v)
+    s = stem.stem_score(p, qd, kd, vd)
+    kcap = 12                                     # max_nb: every row could hold all its blocks
+    idx, cnt = stem.stem_schedule_topk(p, s, [3], 0.5, 1.0, 1, 1, kcap)
+    ri, rc = O.schedule_topk(s.cpu().numpy(), cu, [3], 0.5, 1.0, 1, 1, kcap)
+    lists_equal(idx.cpu().numpy(), cnt.cpu().numpy(), ri, rc, "spare capacity")
+    ig, cg = idx.cpu().numpy(), cnt.cpu().numpy()
+    for h in range(2):
+        for r in range(12):
+            assert np.all(ig[h, r, cg[h, r]:] == -1)
+    out = stem.stem_bsa_prefill(p, qd, kd, vd, idx, cnt, SCALE)
+    ro, _ = O.block_sparse_attention(qf, kf, vf, ri, rc, cu, 2, 1, SCALE)
+    check_out(f64(out), ro, BF16_MAX_ABS, BF16_MEAN_REL, "spare capacity")
