@@ -37,7 +37,8 @@ DEFAULTS = dict(block_size=128, stride=8, chunk_size=2048, norm=1.0,
 
 EXPORTED = ("stem_status_string", "stem_score_workspace_bytes", "stem_score",
             "stem_schedule_topk", "stem_tpd_budget", "stem_kept_count", "stem_max_kept",
-            "stem_attn_workspace_bytes", "stem_bsa_prefill", "stem_dense_prefill")
+            "stem_attn_workspace_bytes", "stem_bsa_prefill", "stem_dense_prefill",
+            "stem_bsa_prefill_paged")
 
 
 class StemError(RuntimeError):
@@ -88,6 +89,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.stem_bsa_prefill.restype = ctypes.c_int
     lib.stem_dense_prefill.argtypes = [P, i32, vp, vp, vp, vp, vp, vp, f32, vp, vp, vp, sz, vp]
     lib.stem_dense_prefill.restype = ctypes.c_int
+    lib.stem_bsa_prefill_paged.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, i32, f32, vp, vp,
+                                           vp, sz, vp]
+    lib.stem_bsa_prefill_paged.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -256,6 +260,54 @@ def stem_bsa_prefill(p: Problem, q, k, v, block_idx, block_cnt, softmax_scale: O
                               _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                               _stream(stream))
     _check("stem_bsa_prefill", st)
+    return (out, lse) if lse is not None else out
+
+
+def stem_bsa_prefill_paged(p: Problem, q, k_pages, v_pages, block_table, block_idx, block_cnt,
+                           softmax_scale: Optional[float] = None, scales=None,
+                           out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                           want_lse: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
+    """Block-sparse fp8 attention with K/V in a page pool.
+
+    q: e4m3 [T][Hq][d]; k_pages, v_pages: e4m3 [num_pages][128][Hkv][d];
+    block_table: int32 [num_seqs][table_stride] (page of key block J of sequence z);
+    scales = (q_scale [R][Hq], k_scale [num_pages][Hkv], v_scale [num_pages][Hkv]).
+    """
+    lib = load_library()
+    q8 = q.view(torch.uint8) if q.dtype == torch.float8_e4m3fn else q
+    kp = k_pages.view(torch.uint8) if k_pages.dtype == torch.float8_e4m3fn else k_pages
+    vpg = v_pages.view(torch.uint8) if v_pages.dtype == torch.float8_e4m3fn else v_pages
+    _need(q8, "q", torch.uint8, (p.T, p.Hq, p.d))
+    n_pages = int(kp.shape[0])
+    _need(kp, "k_pages", torch.uint8, (n_pages, 128, p.Hkv, p.d))
+    _need(vpg, "v_pages", torch.uint8, (n_pages, 128, p.Hkv, p.d))
+    if scales is None or len(scales) != 3:
+        raise ValueError("paged fp8 attention needs (q_scale, k_scale, v_scale)")
+    qs, kss, vs = scales
+    _need(qs, "q_scale", torch.float32, (p.R, p.Hq))
+    _need(kss, "k_scale", torch.float32, (n_pages, p.Hkv))
+    _need(vs, "v_scale", torch.float32, (n_pages, p.Hkv))
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != len(p.nbs) \
+            or not block_table.is_contiguous():
+        raise ValueError("block_table: expected contiguous int32 [num_seqs][table_stride]")
+    _need(block_cnt, "block_cnt", torch.int32, (p.Hq, p.R))
+    if block_idx.dtype != torch.int32 or block_idx.dim() != 3 or tuple(block_idx.shape[:2]) != (p.Hq, p.R) \
+            or not block_idx.is_contiguous():
+        raise ValueError("block_idx: expected contiguous int32 [Hq][R][k_cap]")
+    scale = 1.0 / math.sqrt(p.d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((p.T, p.Hq, p.d), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (p.T, p.Hq, p.d))
+    if want_lse and lse is None:
+        lse = torch.empty((p.Hq, p.T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (p.Hq, p.T))
+    ws = _attn_workspace(p, STEM_DTYPE_FP8_E4M3, workspace, q.device)
+    st = lib.stem_bsa_prefill_paged(p.ref, _ptr(q8), _ptr(kp), _ptr(vpg), _ptr(qs), _ptr(kss), _ptr(vs),
+                                    _ptr(block_table), int(block_table.shape[1]), n_pages, _ptr(block_idx),
+                                    _ptr(block_cnt), int(block_idx.shape[2]), scale, _ptr(out), _ptr(lse),
+                                    _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _check("stem_bsa_prefill_paged", st)
     return (out, lse) if lse is not None else out
 
 

@@ -129,16 +129,16 @@ __global__ __launch_bounds__(256) void vprep_bf16_kernel(const __bf16 *__restric
 
 // fp8: writes the e4m3 V^T image (16 KB per block) and an fp16 V^T image
 // (32 KB per block, exact) used when the block is a row's diagonal block.
-__global__ __launch_bounds__(256) void vprep_fp8_kernel(const uint8_t *__restrict__ v,
-                                                        uint8_t *__restrict__ img8,
-                                                        uint16_t *__restrict__ img16, int Hkv, int R) {
+// Block kb (global key-block row, the image index) starts at token tb of v.
+__device__ __forceinline__ void vprep_fp8_block(const uint8_t *__restrict__ v, size_t tb, int kb, int g,
+                                                uint8_t *__restrict__ img8, uint16_t *__restrict__ img16,
+                                                int Hkv, int R, uint8_t *tile) {
   constexpr int RS = kHeadDim + 16;
-  __shared__ __attribute__((aligned(16))) uint8_t tile[kBlock * RS];
-  const int kb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int key = (tid >> 3) + 32 * p, ch = tid & 7;
-    st16(&tile[key * RS + 16 * ch], ld16(v + (((size_t)kb * kBlock + key) * Hkv + g) * kHeadDim + 16 * ch));
+    st16(&tile[key * RS + 16 * ch], ld16(v + ((tb + key) * Hkv + g) * kHeadDim + 16 * ch));
   }
   __syncthreads();
   uint8_t *o8 = img8 + ((size_t)g * R + kb) * kTile8;
@@ -170,6 +170,29 @@ __global__ __launch_bounds__(256) void vprep_fp8_kernel(const uint8_t *__restric
     st16(o16 + d * kRow16 + 8 * ch, u32x4{w4[0], w4[1], w4[2], w4[3]});
   }
   if (tid < kBlock) st16(o16 + tid * kRow16 + kHeadDim, u32x4{0u, 0u, 0u, 0u});
+}
+
+__global__ __launch_bounds__(256) void vprep_fp8_kernel(const uint8_t *__restrict__ v,
+                                                        uint8_t *__restrict__ img8,
+                                                        uint16_t *__restrict__ img16, int Hkv, int R) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kBlock * (kHeadDim + 16)];
+  const int kb = blockIdx.x, g = blockIdx.y;
+  vprep_fp8_block(v, (size_t)kb * kBlock, kb, g, img8, img16, Hkv, R, tile);
+}
+
+// Paged: row kb_local of this launch's sequences reads its tokens from the
+// page its sequence's table names (clamped into the pool).
+__global__ __launch_bounds__(256) void vprep_fp8_paged_kernel(const uint8_t *__restrict__ v,
+                                                              uint8_t *__restrict__ img8,
+                                                              uint16_t *__restrict__ img16, int Hkv, int R,
+                                                              const int32_t *__restrict__ table,
+                                                              int table_stride, int num_pages, SeqTable t) {
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kBlock * (kHeadDim + 16)];
+  const int kb = t.row[0] + blockIdx.x, g = blockIdx.y;
+  const int z = seq_of(t.row, t.n, kb);
+  int page = table[(size_t)(t.z0 + z) * table_stride + (kb - t.row[z])];
+  page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+  vprep_fp8_block(v, (size_t)page * kBlock, kb, g, img8, img16, Hkv, R, tile);
 }
 
 // ============================================================ work decode
@@ -582,6 +605,14 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
     return;
   }
   auto clampJ = [&](int x) { return x < 0 ? 0 : (x > w.I ? w.I : x); };
+  // Key-block row of block J in K, V and their scales: its page when K/V
+  // are paged (clamped into the pool), else its packed row.
+  cint32 *ptab = a.table ? as_const(a.table) + (size_t)(t.z0 + w.z) * a.table_stride : nullptr;
+  auto srow = [&](int J) {
+    if (!ptab) return zrow + J;
+    const int pg = ptab[J];
+    return pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+  };
 
   i32x8 qf[2];
   {
@@ -607,11 +638,11 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
     const int r = sl / 9, ch = sl - 9 * (sl / 9);
     koff[m] = (uint32_t)(r * kstride + 16 * (ch < 8 ? ch : 0));
   }
-  const uint8_t *kbase = kp + (ztok * a.Hkv + w.g) * kHeadDim;
+  const uint8_t *kbase = kp + (size_t)w.g * kHeadDim;
   const uint8_t *v8base = a.vimg8 + ((size_t)w.g * a.R + zrow) * kTile8 + lane * 16;
   const uint16_t *v16base = a.vimg16 + ((size_t)w.g * a.R + zrow) * kTile16 + lane * 8;
   auto issue_k = [&](int J) __attribute__((always_inline)) {
-    const uint8_t *src = kbase + (size_t)J * kBlock * kstride;
+    const uint8_t *src = kbase + (size_t)srow(J) * kBlock * kstride;
 #pragma unroll
     for (int m = 0; m < 5; ++m)
       if (m < nk8) __builtin_amdgcn_global_load_lds(src + koff[m], lds_ptr(Ks + (wv + 4 * m) * 1024), 16, 0, 0);
@@ -652,8 +683,9 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
     if (v16_pending) wait_vmcnt<8>(); else wait_vmcnt<4>();
     block_sync();
     const bool diag = may_diag && (J == w.I);
-    const float c = cq * a.k_scale[(size_t)(zrow + J) * a.Hkv + w.g];
-    const float vs = a.v_scale[(size_t)(zrow + J) * a.Hkv + w.g];
+    const int sr = srow(J);
+    const float c = cq * a.k_scale[(size_t)sr * a.Hkv + w.g];
+    const float vs = a.v_scale[(size_t)sr * a.Hkv + w.g];
     f32x16 s[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -754,6 +786,13 @@ hipError_t launch_vprep(const AttnLaunch &a, bool fp8, hipStream_t s) {
                        a.Hkv, a.R);
   else
     hipLaunchKernelGGL(vprep_bf16_kernel, grid, dim3(256), 0, s, (const __bf16 *)a.v, a.vimg16, a.Hkv, a.R);
+  return hipGetLastError();
+}
+
+hipError_t launch_vprep_paged(const AttnLaunch &a, const SeqTable &t, int rows, hipStream_t s) {
+  const dim3 grid(rows, a.Hkv);
+  hipLaunchKernelGGL(vprep_fp8_paged_kernel, grid, dim3(256), 0, s, (const uint8_t *)a.v, a.vimg8, a.vimg16, a.Hkv,
+                     a.R, a.table, a.table_stride, a.num_pages, t);
   return hipGetLastError();
 }
 

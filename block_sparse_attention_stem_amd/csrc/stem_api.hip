@@ -45,6 +45,7 @@ int check_problem(const stem_problem_t *p, Shape *s) {
 void fill_table(const stem_problem_t *p, int z0, int n, SeqTable *t) {
   memset(t, 0, sizeof(*t));
   t->n = n;
+  t->z0 = z0;
   for (int i = 0; i <= n; ++i) {
     t->tok[i] = p->cu_seqlens_host[z0 + i];
     t->row[i] = t->tok[i] / kBlock;
@@ -212,7 +213,8 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
                        const void *v, const float *q_scale, const float *k_scale,
                        const float *v_scale, const int32_t *block_idx, const int32_t *block_cnt,
                        int32_t k_cap, float softmax_scale, void *out, float *lse, void *workspace,
-                       size_t workspace_bytes, void *stream, bool sparse) {
+                       size_t workspace_bytes, void *stream, bool sparse,
+                       const int32_t *table = nullptr, int32_t table_stride = 0, int32_t num_pages = 0) {
   Shape s;
   int st = check_problem(p, &s);
   if (st != STEM_OK) return st;
@@ -256,14 +258,18 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
   a.R = s.R;
   a.T = s.T;
   a.scale_log2 = (float)((double)softmax_scale * 1.4426950408889634);
+  a.table = table;
+  a.table_stride = table_stride;
+  a.num_pages = num_pages;
   hipStream_t hs = as_stream(stream);
-  if (launch_vprep(a, fp8, hs) != hipSuccess) return STEM_ERR_HIP;
+  if (!table && launch_vprep(a, fp8, hs) != hipSuccess) return STEM_ERR_HIP;
   for (int z0 = 0; z0 < s.B; z0 += kMaxSeqsPerLaunch) {
     const int n = s.B - z0 < kMaxSeqsPerLaunch ? s.B - z0 : kMaxSeqsPerLaunch;
     SeqTable t;
     fill_table(p, z0, n, &t);
     const int rows = t.row[n] - t.row[0];
     if ((int64_t)rows * s.Hq >= ((int64_t)1 << 31)) return STEM_ERR_UNSUPPORTED;
+    if (table && launch_vprep_paged(a, t, rows, hs) != hipSuccess) return STEM_ERR_HIP;
     if (launch_attn(a, t, rows, sparse, fp8, hs) != hipSuccess) return STEM_ERR_HIP;
   }
   return STEM_OK;
@@ -284,6 +290,21 @@ int stem_dense_prefill(const stem_problem_t *p, int32_t dtype, const void *q, co
                        void *workspace, size_t workspace_bytes, void *stream) {
   return attn_common(p, dtype, q, k, v, q_scale, k_scale, v_scale, nullptr, nullptr, 0,
                      softmax_scale, out, lse, workspace, workspace_bytes, stream, false);
+}
+
+int stem_bsa_prefill_paged(const stem_problem_t *p, const void *q, const void *k_pages,
+                           const void *v_pages, const float *q_scale, const float *k_scale_pages,
+                           const float *v_scale_pages, const int32_t *block_table,
+                           int32_t table_stride, int32_t num_pages, const int32_t *block_idx,
+                           const int32_t *block_cnt, int32_t k_cap, float softmax_scale, void *out,
+                           float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+  Shape s;
+  const int st = check_problem(p, &s);
+  if (st != STEM_OK) return st;
+  if (!block_table || num_pages < 1 || table_stride < s.max_nb) return STEM_ERR_INVALID_ARG;
+  return attn_common(p, STEM_DTYPE_FP8_E4M3, q, k_pages, v_pages, q_scale, k_scale_pages, v_scale_pages,
+                     block_idx, block_cnt, k_cap, softmax_scale, out, lse, workspace, workspace_bytes, stream,
+                     true, block_table, table_stride, num_pages);
 }
 
 }  // extern "C"

@@ -19,6 +19,7 @@ constexpr int kMaxRowBlocks = 2048;   // top-k row length limit (256K tokens)
 // item[z] is a per-kernel prefix of work items (set by the launcher).
 struct SeqTable {
   int32_t n;
+  int32_t z0;                       // global index of the launch's first sequence
   int32_t tok[kMaxSeqsPerLaunch + 1];
   int32_t row[kMaxSeqsPerLaunch + 1];
   int32_t item[kMaxSeqsPerLaunch + 1];
@@ -134,10 +135,18 @@ struct AttnLaunch {
   uint8_t *vimg8;                // workspace (fp8 only): e4m3 V^T tile images [Hkv][R][128 x 144 B]
   int32_t Hq, Hkv, R, T;
   float scale_log2;              // softmax_scale * log2(e)
+  // Paged K/V (fp8 only; null table = contiguous varlen tensors): k and v
+  // point at pools of num_pages pages of kBlock tokens, [page][token][Hkv][d];
+  // table[z * table_stride + J] is the page of key block J of sequence z;
+  // k_scale / v_scale are then [page][Hkv].
+  const int32_t *table;
+  int32_t table_stride, num_pages;
 };
 size_t attn_workspace_bytes(int Hkv, int R, bool fp8);
 size_t attn_workspace_img16_offset(int Hkv, int R);
 hipError_t launch_vprep(const AttnLaunch &a, bool fp8, hipStream_t s);
+// Paged pre-pass for the rows of one launch's sequences.
+hipError_t launch_vprep_paged(const AttnLaunch &a, const SeqTable &t, int rows_in_launch, hipStream_t s);
 hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows_in_launch,
                        bool sparse, bool fp8, hipStream_t s);
 

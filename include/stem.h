@@ -186,6 +186,32 @@ int stem_dense_prefill(const stem_problem_t *p, int32_t dtype, const void *q, co
                        const float *v_scale, float softmax_scale, void *out, float *lse,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Block-sparse attention on a paged fp8 K/V cache (the AngelSlim doc's
+ * "paged" fp8 execution path, §6 parameter table: hpc_fp8_path; §3 support
+ * table).  The pages name the path but not its layout; this reading keeps
+ * everything as in stem_bsa_prefill with STEM_DTYPE_FP8_E4M3 except where K
+ * and V live:
+ * q, q_scale: as stem_bsa_prefill (packed varlen e4m3 [T][Hq][d], fp32 [R][Hq]).
+ * k_pages, v_pages: e4m3 pools of num_pages pages of block_size tokens,
+ *   [page][token][Hkv][d] (one page per 128-token key block).
+ * k_scale_pages, v_scale_pages: fp32 [num_pages][Hkv], per page and KV head.
+ * block_table: device int32 [num_seqs][table_stride]; entry [z][J] is the
+ *   page holding key block J of sequence z, for J < nb_z.  Entries outside
+ *   [0, num_pages) are clamped into it (never read out of the pool).
+ * block_idx, block_cnt, k_cap, softmax_scale, out, lse, workspace: as
+ *   stem_bsa_prefill (workspace: stem_attn_workspace_bytes(p, FP8)).
+ * Errors: INVALID_ARG for a null table, num_pages < 1 or table_stride below
+ *   the longest sequence's block count, plus those of stem_bsa_prefill.
+ * The result equals stem_bsa_prefill on the same blocks laid out contiguously.
+ * ------------------------------------------------------------------------- */
+int stem_bsa_prefill_paged(const stem_problem_t *p, const void *q, const void *k_pages,
+                           const void *v_pages, const float *q_scale, const float *k_scale_pages,
+                           const float *v_scale_pages, const int32_t *block_table,
+                           int32_t table_stride, int32_t num_pages, const int32_t *block_idx,
+                           const int32_t *block_cnt, int32_t k_cap, float softmax_scale, void *out,
+                           float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

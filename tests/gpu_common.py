@@ -104,3 +104,30 @@ def quantize_fp8(q, k, v, seqlens):
 
 def dequant(codes, scales):
     return O.dequantize_blocks(codes.numpy(), scales.numpy(), 128)
+
+
+def page_pool(k8, v8, ks, vs, seqlens, spare=7, seed=0):
+    """Scatter the per-block e4m3 K/V codes and scales of packed sequences
+    into a shuffled page pool with `spare` unused pages filled with NaN codes
+    (0x7F) and NaN scales, so that any read of a wrong page shows up.
+    Returns (k_pages, v_pages, k_scale_pages, v_scale_pages, table), CPU."""
+    T, Hkv, d = k8.shape
+    R = T // 128
+    n_pages = R + spare
+    perm = torch.randperm(n_pages, generator=torch.Generator().manual_seed(seed))
+    kp = torch.full((n_pages, 128, Hkv, d), 0x7F, dtype=torch.uint8)
+    vp = torch.full((n_pages, 128, Hkv, d), 0x7F, dtype=torch.uint8)
+    ksp = torch.full((n_pages, Hkv), float("nan"), dtype=torch.float32)
+    vsp = torch.full((n_pages, Hkv), float("nan"), dtype=torch.float32)
+    kp[perm[:R]] = k8.reshape(R, 128, Hkv, d)
+    vp[perm[:R]] = v8.reshape(R, 128, Hkv, d)
+    ksp[perm[:R]] = ks
+    vsp[perm[:R]] = vs
+    nbs = [int(n) // 128 for n in seqlens]
+    stride = max(nbs) + 3
+    table = torch.full((len(nbs), stride), -5, dtype=torch.int32)   # unused columns hold garbage
+    r = 0
+    for z, nb in enumerate(nbs):
+        table[z, :nb] = perm[r:r + nb].to(torch.int32)
+        r += nb
+    return kp, vp, ksp, vsp, table

@@ -140,6 +140,26 @@ def test_attention_argument_errors():
     assert stem.stem_attn_workspace_bytes(p, 5) == 0
 
 
+def test_paged_attention_argument_errors():
+    """Every call below carries one invalid argument, so nothing is launched."""
+    lib = stem.load_library()
+    p = stem.Problem([0, 1024], 4, 2)                 # 8 key blocks
+    f = FAKE
+    W = 1 << 30
+    call = lib.stem_bsa_prefill_paged
+    # null table, empty pool, table rows shorter than the longest sequence
+    assert call(p.ref, f, f, f, f, f, f, None, 8, 16, f, f, 8, 0.1, f, None, f, W, None) == 1
+    assert call(p.ref, f, f, f, f, f, f, f, 8, 0, f, f, 8, 0.1, f, None, f, W, None) == 1
+    assert call(p.ref, f, f, f, f, f, f, f, 7, 16, f, f, 8, 0.1, f, None, f, W, None) == 1
+    # fp8 scales are required; lists are required; workspace size
+    assert call(p.ref, f, f, f, None, f, f, f, 8, 16, f, f, 8, 0.1, f, None, f, W, None) == 1
+    assert call(p.ref, f, f, f, f, f, f, f, 8, 16, None, f, 8, 0.1, f, None, f, W, None) == 1
+    assert call(p.ref, f, f, f, f, f, f, f, 8, 16, f, f, 8, 0.1, f, None, f, 100, None) == 4
+    # a ragged sequence length is reported before anything else
+    bad = stem.Problem([0, 1000], 4, 2)
+    assert call(bad.ref, f, f, f, f, f, f, f, 8, 16, f, f, 8, 0.1, f, None, f, W, None) == 2
+
+
 def test_package_defaults_match_the_doc_table():
     import json
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "stem_doc_defaults.json")))

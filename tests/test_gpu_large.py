@@ -22,7 +22,7 @@ import block_sparse_attention_stem_amd as stem
 import oracle as O
 import stem_synth as S
 from gpu_common import (BF16_MAX_ABS, BF16_MEAN_REL, FP8_MAX_ABS, check_lse, check_out,
-                        check_scores, dev, lists_equal, note, to_dev)
+                        check_scores, dev, lists_equal, note, page_pool, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -88,10 +88,23 @@ def _run(w, fp8):
         ref_inputs = None
     note(f"[{w.name}] {'fp8' if fp8 else 'bf16'} block-sparse and dense attention")
     stem.stem_bsa_prefill(p, qa, ka, va, idx, cnt, SCALE, scales=scales, out=out, lse=lse, workspace=aws)
+    paged_equal = None
+    if fp8:
+        # the same layer from a shuffled page pool must give the same bits
+        kp, vp, ksp, vsp, table = page_pool(k8, v8, ks, vs, w.seqlens, spare=5, seed=w.seed)
+        kpd, vpd, tabd = to_dev(kp, vp, table)
+        pout = torch.empty_like(out)
+        plse = torch.empty_like(lse)
+        stem.stem_bsa_prefill_paged(p, qa, kpd, vpd, tabd, idx, cnt, SCALE, scales=to_dev(qs, ksp, vsp),
+                                    out=pout, lse=plse, workspace=aws)
+        torch.cuda.synchronize()
+        paged_equal = bool(torch.equal(pout, out)) and bool(torch.equal(plse, lse))
+        note(f"[{w.name}] paged ({kp.shape[0]} pages) equals contiguous: {paged_equal}")
+        del kpd, vpd, tabd, pout, plse
     stem.stem_dense_prefill(p, qa, ka, va, SCALE, scales=scales, out=dout, workspace=aws)
     torch.cuda.synchronize()
     rows = _sample_rows(w)
-    res = dict(w=w, p=p, kcap=kcap, rows=rows,
+    res = dict(w=w, p=p, kcap=kcap, rows=rows, paged_equal=paged_equal,
                scores=scores.cpu().numpy(), idx=idx.cpu().numpy(), cnt=cnt.cpu().numpy(),
                out=_gather_rows(out, rows), dout=_gather_rows(dout, rows),
                lse={(hi, r): lse[h, r * 128:(r + 1) * 128].to(torch.float64).cpu().numpy()
@@ -175,3 +188,11 @@ def test_dense_attention_on_sampled_rows(big):
                                          heads=[hi], q_range=(t0, t0 + 128))
         check_out(big["dout"][(hi, r)], ro[a + t0:a + t0 + 128, hi, :], bar[0], bar[1],
                   f"{w.name} dense head {HS[hi]} row {r}")
+
+
+def test_fp8_paged_equals_contiguous_at_full_size(big):
+    """Paged K/V (shuffled pool, NaN-filled spare pages) reproduce the
+    contiguous fp8 output and LSE bit for bit over the whole layer."""
+    if big["paged_equal"] is None:
+        pytest.skip("bf16 layer: the paged path is fp8 only")
+    assert big["paged_equal"]

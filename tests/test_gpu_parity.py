@@ -16,7 +16,7 @@ import oracle as O
 import stem_synth as S
 from gpu_common import (BF16_MAX_ABS, BF16_MEAN_REL, FP8_MAX_ABS, check_lse, check_out,
                         check_scores, dequant, dev, f64, lists_equal, make_inputs, note,
-                        quantize_fp8, to_dev)
+                        page_pool, quantize_fp8, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -303,3 +303,37 @@ def test_lists_with_spare_capacity_are_padded():
     out = stem.stem_bsa_prefill(p, qd, kd, vd, idx, cnt, SCALE)
     ro, _ = O.block_sparse_attention(qf, kf, vf, ri, rc, cu, 2, 1, SCALE)
     check_out(f64(out), ro, BF16_MAX_ABS, BF16_MEAN_REL, "spare capacity")
+
+
+# ------------------------------------------------------------ paged fp8 ----
+
+def test_fp8_paged_matches_oracle_and_contiguous(fp8_small):
+    """K/V scattered over a shuffled page pool (spare pages hold NaN codes):
+    the paged kernel matches the oracle on the dequantised contiguous tensors
+    and reproduces the contiguous fp8 path bit for bit."""
+    lens, (q, k, v), (q8, k8, v8), (qs, ks, vs), (qf, kf, vf) = fp8_small
+    cu = S.cu_from_lengths(lens)
+    p = stem.Problem(cu, 4, 2)
+    qd, kd, vd = to_dev(q, k, v)
+    s = stem.stem_score(p, qd, kd, vd)
+    idx, cnt = stem.stem_schedule_topk(p, s, [1, 3, 4], 0.5, 1.0, 1, 1)
+    ri, rc = idx.cpu().numpy(), cnt.cpu().numpy()
+    kp, vp, ksp, vsp, table = page_pool(k8, v8, ks, vs, lens, spare=7, seed=21)
+    note(f"  pool of {kp.shape[0]} pages, table stride {table.shape[1]}")
+    sc_paged = to_dev(qs, ksp, vsp)
+    q8d, kpd, vpd, tabd = to_dev(q8, kp, vp, table)
+    out, lse = stem.stem_bsa_prefill_paged(p, q8d, kpd, vpd, tabd, idx, cnt, SCALE, scales=sc_paged,
+                                           want_lse=True)
+    ro, rl = O.block_sparse_attention(qf, kf, vf, ri, rc, cu, 4, 2, SCALE)
+    check_out(f64(out), ro, FP8_MAX_ABS, None, "fp8 paged bsa")
+    check_lse(lse.cpu().numpy().astype(np.float64), rl, "fp8 paged bsa")
+    ref_out, ref_lse = stem.stem_bsa_prefill(p, *to_dev(q8, k8, v8), idx, cnt, SCALE,
+                                             scales=to_dev(qs, ks, vs), want_lse=True)
+    assert torch.equal(out, ref_out), "paged and contiguous fp8 outputs differ"
+    assert torch.equal(lse, ref_lse)
+    # every block listed: the paged path equals dense attention
+    fi, fc = O.full_lists(cu, 4)
+    fout = stem.stem_bsa_prefill_paged(p, q8d, kpd, vpd, tabd, *to_dev(torch.from_numpy(fi), torch.from_numpy(fc)),
+                                       SCALE, scales=sc_paged)
+    do, _ = O.dense_causal_attention(qf, kf, vf, cu, 4, 2, SCALE)
+    check_out(f64(fout), do, FP8_MAX_ABS, None, "fp8 paged all blocks")
