@@ -324,7 +324,10 @@ def fp8_varlen(args, torch, stem, S, dev):
     qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
     qa, ka, va = q8.to(dev), k8.to(dev), v8.to(dev)
     scl = (qs.to(dev), ks.to(dev), vs.to(dev))
-    del q, k, v, q8, k8, v8
+    pool = page_pool(torch, k8, v8, ks, vs, w_hi.seqlens, seed=1)
+    kpd, vpd, tabd = pool[0].to(dev), pool[1].to(dev), pool[4].to(dev)
+    pscl = (scl[0], pool[2].to(dev), pool[3].to(dev))
+    del q, k, v, q8, k8, v8, pool
     scores = torch.empty((p.Hq, p.R, p.max_nb), dtype=torch.float32, device=dev)
     ws = torch.empty(stem.stem_score_workspace_bytes(p), dtype=torch.uint8, device=dev)
     aws = torch.empty(stem.stem_attn_workspace_bytes(p, stem.STEM_DTYPE_FP8_E4M3), dtype=torch.uint8,
@@ -332,7 +335,7 @@ def fp8_varlen(args, torch, stem, S, dev):
     out = torch.empty((p.T, p.Hq, 128), dtype=torch.bfloat16, device=dev)
     flop_dense = dense_flop(w_hi.seqlens, w_hi.num_q_heads)
     dense_pairs = p.Hq * sum(L * (L + 1) / 2 for L in w_hi.seqlens)
-    layers = {}
+    layers, lists = {}, {}
     for tag, w in (("alpha_1.0", w_hi), ("alpha_0.7", w_lo)):
         kcap = stem.stem_max_kept(p, w.k_start, w.mu, w.alpha, w.n_init, w.n_window)
         idx = torch.empty((p.Hq, p.R, kcap), dtype=torch.int32, device=dev)
@@ -349,6 +352,7 @@ def fp8_varlen(args, torch, stem, S, dev):
         torch.cuda.synchronize()
         for ev in evs:
             timer.collect(ev)
+        lists[tag] = (idx, cnt)
         pairs = bsa_pairs(idx, cnt, p)
         t_layer = timer.mean("score") + timer.mean("schedule") + timer.mean("bsa")
         layers[tag] = {"ms": t_layer, "stages_ms": {n: timer.mean(n) for n in ("score", "schedule", "bsa")},
@@ -357,8 +361,11 @@ def fp8_varlen(args, torch, stem, S, dev):
                        "effective_tflops": flop_dense / (t_layer * 1e-3) / 1e12}
         log(f"[bench]   fp8 {tag}: layer {t_layer:.2f} ms (bsa {timer.mean('bsa'):.2f} ms, "
             f"rho {pairs / dense_pairs:.4f})")
-    dtimer = StageTimer(torch, ["dense"])
-    dfn = [lambda: stem.stem_dense_prefill(p, qa, ka, va, scales=scl, out=out, workspace=aws)]
+    idx, cnt = lists["alpha_0.7"]
+    dtimer = StageTimer(torch, ["dense", "paged"])
+    dfn = [lambda: stem.stem_dense_prefill(p, qa, ka, va, scales=scl, out=out, workspace=aws),
+           lambda: stem.stem_bsa_prefill_paged(p, qa, kpd, vpd, tabd, idx, cnt, scales=pscl, out=out,
+                                               workspace=aws)]
     dtimer.run(dfn)
     torch.cuda.synchronize()
     devs = [dtimer.run(dfn) for _ in range(3)]
@@ -367,6 +374,11 @@ def fp8_varlen(args, torch, stem, S, dev):
         dtimer.collect(ev)
     t_dense = dtimer.mean("dense")
     lo = layers["alpha_0.7"]
+    t_paged = dtimer.mean("paged")
+    lo["paged_bsa_ms"] = t_paged
+    lo["paged_vs_contiguous"] = t_paged / lo["stages_ms"]["bsa"]
+    log(f"[bench]   fp8 alpha_0.7 paged ({kpd.shape[0]} shuffled pages): bsa {t_paged:.2f} ms "
+        f"({lo['paged_vs_contiguous']:.3f}x contiguous)")
     for L_ in layers.values():
         L_["skip_overhead"] = L_["stages_ms"]["bsa"] / (L_["computed_pair_fraction"] * t_dense) - 1.0
     total = 5 * layers["alpha_1.0"]["ms"] + 31 * lo["ms"]
@@ -380,6 +392,31 @@ def fp8_varlen(args, torch, stem, S, dev):
             "roofline": {"bound": "mfma", "kernel": "attn_fp8_kernel<sparse>", "achieved": lo["bsa_tflops"],
                          "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                          "frac": lo["bsa_tflops"] / PEAK_FP8_TFLOPS}}
+
+
+def page_pool(torch, k8, v8, ks, vs, seqlens, seed=0, spare=3):
+    """Scatter the contiguous fp8 K/V blocks into a pool of 128-token pages
+    in shuffled order plus a few unused pages, and build the per-sequence
+    block table that names them (data movement only, done outside the
+    timed region)."""
+    nbs = [L // 128 for L in seqlens]
+    R, Hkv, d = sum(nbs), k8.shape[1], k8.shape[2]
+    g = torch.Generator().manual_seed(seed)
+    perm = torch.randperm(R + spare, generator=g)[:R]      # page of contiguous block r
+    kp = torch.zeros((R + spare, 128, Hkv, d), dtype=k8.dtype)
+    vp = torch.zeros_like(kp)
+    ksp = torch.ones((R + spare, Hkv), dtype=ks.dtype)
+    vsp = torch.ones_like(ksp)
+    kp[perm] = k8.reshape(R, 128, Hkv, d)
+    vp[perm] = v8.reshape(R, 128, Hkv, d)
+    ksp[perm] = ks
+    vsp[perm] = vs
+    table = torch.zeros((len(seqlens), max(nbs)), dtype=torch.int32)
+    r0 = 0
+    for z, nb in enumerate(nbs):
+        table[z, :nb] = perm[r0:r0 + nb].to(torch.int32)
+        r0 += nb
+    return kp, vp, ksp, vsp, table
 
 
 def kstart_for_density(stem, nb, target, alpha=0.7, mu=0.5, n_init=1, n_window=2):
