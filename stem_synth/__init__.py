@@ -138,6 +138,53 @@ def make_workload_qkv(w: Workload, dtype: torch.dtype = torch.bfloat16):
     return make_qkv(w.seqlens, w.num_q_heads, w.num_kv_heads, w.head_dim, w.seed, w.sink, dtype)
 
 
+def make_topic_qkv(seqlens: Sequence[int], num_q_heads: int, num_kv_heads: int,
+                   head_dim: int = 128, seed: int = 0, topics: int = 8, gain: float = 6.0,
+                   value_sigma: float = 0.5, block_size: int = BLOCK,
+                   dtype: torch.dtype = torch.float64):
+    """Q, K, V ([T][H][d]) with planted block-level attention structure.
+
+    Recipe, per sequence and KV head: `topics` random unit directions; every
+    key block takes one of them at random and adds `gain` times it to each of
+    its keys; every value block is scaled by exp(value_sigma * N(0, 1)).  Per
+    query head, every query block adds `gain` times the direction of one
+    uniformly drawn causal key block (itself included).  With gain 6 and
+    d = 128 a same-topic key scores about gain^2 / sqrt(d) = 3.2 nats above the
+    rest, so attention concentrates on the matching blocks, unlike the plain
+    Gaussian draw of `make_qkv`, where it is nearly flat.  Base draws are
+    N(0, 1) as in `make_qkv`.
+    """
+    T = int(sum(seqlens))
+    grp = num_q_heads // num_kv_heads
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    q = torch.randn(T, num_q_heads, head_dim, generator=g, dtype=torch.float64)
+    k = torch.randn(T, num_kv_heads, head_dim, generator=g, dtype=torch.float64)
+    v = torch.randn(T, num_kv_heads, head_dim, generator=g, dtype=torch.float64)
+    start = 0
+    for n in seqlens:
+        n = int(n)
+        assert n % block_size == 0
+        nb = n // block_size
+        c = torch.randn(num_kv_heads, topics, head_dim, generator=g, dtype=torch.float64)
+        c = c / c.norm(dim=-1, keepdim=True)
+        topic = torch.randint(0, topics, (num_kv_heads, nb), generator=g)
+        vz = torch.randn(nb, num_kv_heads, generator=g, dtype=torch.float64)
+        pick = torch.rand(num_q_heads, nb, generator=g, dtype=torch.float64)
+        kb = k[start:start + n].view(nb, block_size, num_kv_heads, head_dim)
+        vb = v[start:start + n].view(nb, block_size, num_kv_heads, head_dim)
+        qb = q[start:start + n].view(nb, block_size, num_q_heads, head_dim)
+        heads = torch.arange(num_kv_heads)
+        kb += gain * c[heads[None, :], topic.T][:, None]               # [nb][1][Hkv][d]
+        vb *= torch.exp(value_sigma * vz)[:, None, :, None]
+        src = (pick * (torch.arange(nb, dtype=torch.float64) + 1)).long()   # [Hq][nb], <= I
+        hk = torch.arange(num_q_heads) // grp
+        qtopic = topic[hk[:, None], src]                                # [Hq][nb]
+        qb += gain * c[hk[:, None], qtopic].permute(1, 0, 2)[:, None]   # [nb][1][Hq][d]
+        start += n
+    return q.to(dtype), k.to(dtype), v.to(dtype)
+
+
 def quantize_e4m3_per_block(x: torch.Tensor, seqlens: Sequence[int], block_size: int = BLOCK):
     """Per-(128-token block, head) symmetric e4m3fn quantisation of a [T][H][d] tensor.
 
