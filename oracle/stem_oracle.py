@@ -277,46 +277,52 @@ def schedule_topk(S: np.ndarray, cu_seqlens: Sequence[int], k_start: Sequence, m
 def block_sparse_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, idx: np.ndarray,
                            cnt: np.ndarray, cu_seqlens: Sequence[int], num_q_heads: int,
                            num_kv_heads: int, softmax_scale: float, block_size: int = 128,
-                           rows: Sequence[Tuple[int, int]] = None):
+                           rows: Sequence[Tuple[int, int]] = None, q_block: int = None):
     """O float64 [T][Hq][d] and lse float64 [Hq][T] (natural log).
 
     For each (head h, query block I) gather the key/value tokens of the listed
     blocks, mask keys later than the query, softmax in fp64 and aggregate.  An
     empty list gives O = 0 and lse = -inf.  `rows` restricts the work to the
     listed (h, global q block) pairs (other outputs stay NaN).
+
+    Query blocks have `q_block` tokens (default: `block_size`) and key blocks
+    `block_size` tokens: the rectangular block shapes of the HPC-BSA operators
+    ([HPC] §三.3.1 names 64x128 next to 128x128).  Row I of a sequence covers
+    queries [I q_block, (I+1) q_block); its list holds key-block ids.
     """
     T, _, d = q.shape
+    qb_len = block_size if q_block is None else int(q_block)
     group = num_q_heads // num_kv_heads
     O = np.full((T, num_q_heads, d), np.nan)
     lse = np.full((num_q_heads, T), np.nan)
     seqs = _seq_bounds(cu_seqlens)
     row_seq = []
     for z, (a, b) in enumerate(seqs):
-        for I in range((b - a) // block_size):
+        for I in range((b - a) // qb_len):
             row_seq.append((z, I))
     work = rows if rows is not None else [(h, r) for h in range(num_q_heads) for r in range(len(row_seq))]
     for (h, r) in work:
         z, I = row_seq[r]
         a = seqs[z][0]
         g = h // group
-        q0 = a + I * block_size
-        qb = q[q0:q0 + block_size, h, :].astype(np.float64)
+        q0 = a + I * qb_len
+        qb = q[q0:q0 + qb_len, h, :].astype(np.float64)
         blocks = [int(J) for J in idx[h, r, :int(cnt[h, r])]]
         if not blocks:
-            O[q0:q0 + block_size, h, :] = 0.0
-            lse[h, q0:q0 + block_size] = NEG_INF
+            O[q0:q0 + qb_len, h, :] = 0.0
+            lse[h, q0:q0 + qb_len] = NEG_INF
             continue
         kpos = np.concatenate([np.arange(J * block_size, (J + 1) * block_size) for J in blocks])
         ks = k[a + kpos, g, :].astype(np.float64)
         vs = v[a + kpos, g, :].astype(np.float64)
-        x = softmax_scale * (qb @ ks.T)                              # [128][n]
-        qpos = np.arange(I * block_size, (I + 1) * block_size)[:, None]
+        x = softmax_scale * (qb @ ks.T)                              # [q_block][n]
+        qpos = np.arange(I * qb_len, (I + 1) * qb_len)[:, None]
         x[kpos[None, :] > qpos] = NEG_INF
         mx = x.max(axis=1, keepdims=True)
         p = np.exp(x - mx)
         den = p.sum(axis=1, keepdims=True)
-        O[q0:q0 + block_size, h, :] = (p @ vs) / den
-        lse[h, q0:q0 + block_size] = (mx + np.log(den))[:, 0]
+        O[q0:q0 + qb_len, h, :] = (p @ vs) / den
+        lse[h, q0:q0 + qb_len] = (mx + np.log(den))[:, 0]
     return O, lse
 
 
@@ -357,17 +363,25 @@ def dense_causal_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_seqle
     return O, lse
 
 
-def full_lists(cu_seqlens: Sequence[int], num_q_heads: int, block_size: int = 128):
-    """Every causal block listed (idx, cnt), for the all-kept special case."""
+def full_lists(cu_seqlens: Sequence[int], num_q_heads: int, block_size: int = 128,
+               q_block: int = None):
+    """Every causal block listed (idx, cnt), for the all-kept special case.
+
+    With `q_block`, rows are query blocks of that many tokens; row I lists
+    every key block holding a key <= its last query.
+    """
+    qb_len = block_size if q_block is None else int(q_block)
     seqs = _seq_bounds(cu_seqlens)
-    nbs = [(b - a) // block_size for a, b in seqs]
-    R, maxnb = sum(nbs), max(nbs)
-    idx = np.full((num_q_heads, R, maxnb), -1, dtype=np.int32)
+    nrows = [(b - a) // qb_len for a, b in seqs]
+    R = sum(nrows)
+    last = [((n * qb_len - 1) // block_size) + 1 for n in nrows]
+    idx = np.full((num_q_heads, R, max(last)), -1, dtype=np.int32)
     cnt = np.zeros((num_q_heads, R), dtype=np.int32)
     r = 0
-    for nb in nbs:
-        for I in range(nb):
-            idx[:, r, :I + 1] = np.arange(I + 1)
-            cnt[:, r] = I + 1
+    for n in nrows:
+        for I in range(n):
+            c = ((I + 1) * qb_len - 1) // block_size + 1
+            idx[:, r, :c] = np.arange(c)
+            cnt[:, r] = c
             r += 1
     return idx, cnt

@@ -323,6 +323,89 @@ def test_skipped_blocks_equal_minus_inf_masking():
         row0 += nb
 
 
+def test_half_height_rows_listing_every_block_equal_dense():
+    """P6 for rectangular blocks ([HPC] §三.3.1: 64x128 next to 128x128), here
+    8-query rows against 16-key blocks: listing every block that holds a key
+    <= the row's last query reproduces dense causal attention."""
+    q, k, v, cu = _tiny_qkv(13)
+    idx, cnt = O.full_lists(cu, 4, block_size=16, q_block=8)
+    assert idx.shape[1] == (96 + 64) // 8
+    assert [int(c) for c in cnt[0, :4]] == [1, 1, 2, 2]     # rows 0,1 -> block 0; rows 2,3 -> blocks 0,1
+    Ob, lb = O.block_sparse_attention(q, k, v, idx, cnt, cu, 4, 2, 0.25, block_size=16, q_block=8)
+    Od, ld = O.dense_causal_attention(q, k, v, cu, 4, 2, 0.25)
+    assert np.allclose(Ob, Od, atol=1e-12) and np.allclose(lb, ld, atol=1e-12)
+
+
+def test_half_height_rows_with_the_parent_lists_equal_square_rows():
+    """Both halves of a square row, given the square row's list, see exactly
+    the keys the square row sees: same output and LSE."""
+    q, k, v, cu = _tiny_qkv(14)
+    bs, Hq, Hkv, sc = 16, 4, 2, 0.25
+    r = _rng(15)
+    nbs = [(b - a) // bs for a, b in zip(cu[:-1], cu[1:])]
+    R = sum(nbs)
+    idx = np.full((Hq, R, max(nbs)), -1, np.int32)
+    cnt = np.zeros((Hq, R), np.int32)
+    row = 0
+    for nb in nbs:
+        for I in range(nb):
+            for h in range(Hq):
+                sel = sorted(set(r.choice(I + 1, size=int(r.integers(1, I + 2)), replace=False).tolist()) | {I})
+                idx[h, row, :len(sel)] = sel
+                cnt[h, row] = len(sel)
+            row += 1
+    Os, ls = O.block_sparse_attention(q, k, v, idx, cnt, cu, Hq, Hkv, sc, block_size=bs)
+    Oh, lh = O.block_sparse_attention(q, k, v, np.repeat(idx, 2, axis=1), np.repeat(cnt, 2, axis=1), cu,
+                                      Hq, Hkv, sc, block_size=bs, q_block=bs // 2)
+    assert np.allclose(Oh, Os, atol=1e-12) and np.allclose(lh, ls, atol=1e-12)
+
+
+def test_half_height_rows_equal_token_level_masking():
+    """Rectangular rows with their own random lists (some without the
+    diagonal block, some empty) equal dense attention whose logits are -inf
+    outside the listed (row, block) rectangles; an empty row gives 0."""
+    q, k, v, cu = _tiny_qkv(16)
+    bs, qb, Hq, Hkv, sc = 16, 8, 4, 2, 0.25
+    r = _rng(17)
+    nrows = [(b - a) // qb for a, b in zip(cu[:-1], cu[1:])]
+    R = sum(nrows)
+    idx = np.full((Hq, R, 8), -1, np.int32)
+    cnt = np.zeros((Hq, R), np.int32)
+    row = 0
+    for n in nrows:
+        for I in range(n):
+            top = (I * qb + qb - 1) // bs                # the row's diagonal key block
+            for h in range(Hq):
+                if r.random() < 0.1:
+                    continue                             # empty row
+                sel = sorted(r.choice(top + 1, size=int(r.integers(1, top + 2)), replace=False).tolist())
+                idx[h, row, :len(sel)] = sel
+                cnt[h, row] = len(sel)
+            row += 1
+    assert (cnt == 0).any() and any(cnt[h, i] > 0 and idx[h, i, cnt[h, i] - 1] < (i % 12) * qb // bs
+                                    for h in range(Hq) for i in range(12))
+    Ob, _ = O.block_sparse_attention(q, k, v, idx, cnt, cu, Hq, Hkv, sc, block_size=bs, q_block=qb)
+    row0 = 0
+    for (a, b), n in zip(zip(cu[:-1], cu[1:]), nrows):
+        L = b - a
+        for h in range(Hq):
+            g = h // 2
+            x = sc * (q[a:b, h] @ k[a:b, g].T)
+            mask = np.full((L, L), -np.inf)
+            for I in range(n):
+                for J in idx[h, row0 + I, :cnt[h, row0 + I]]:
+                    mask[I * qb:(I + 1) * qb, J * bs:(J + 1) * bs] = 0.0
+            mask[np.triu_indices(L, 1)] = -np.inf
+            x = x + mask
+            for t in range(L):
+                if np.all(x[t] == -np.inf):
+                    assert np.all(Ob[a + t, h] == 0.0)
+                    continue
+                p = np.exp(x[t] - x[t].max())
+                assert np.allclose(Ob[a + t, h], (p / p.sum()) @ v[a:b, g], atol=1e-12)
+        row0 += n
+
+
 def test_empty_row_gives_zero_and_minus_inf_lse():
     q, k, v, cu = _tiny_qkv(12, L=(32,), Hq=2, Hkv=1, d=8)
     idx = np.full((2, 2, 2), -1, np.int32)
