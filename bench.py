@@ -241,8 +241,13 @@ def run_main(args):
     for ev in evs:
         timer.collect(ev)
 
-    dtimer = StageTimer(torch, ["dense"])
-    dfn = [lambda: stem.stem_dense_prefill(p, qd, kd, vd, out=dout, workspace=aws)]
+    # dense on the same inputs, and the 64 x 128 tile variant on the same
+    # lists (each 64-query half given its row's list: same computed pairs)
+    idx64 = idx.repeat_interleave(2, dim=1).contiguous()
+    cnt64 = cnt.repeat_interleave(2, dim=1).contiguous()
+    dtimer = StageTimer(torch, ["dense", "q64"])
+    dfn = [lambda: stem.stem_dense_prefill(p, qd, kd, vd, out=dout, workspace=aws),
+           lambda: stem.stem_bsa_prefill_q64(p, qd, kd, vd, idx64, cnt64, out=dout, workspace=aws)]
     for _ in range(max(1, args.warmup)):
         dtimer.run(dfn)
     torch.cuda.synchronize()
@@ -250,6 +255,7 @@ def run_main(args):
     torch.cuda.synchronize()
     for ev in devs:
         dtimer.collect(ev)
+    del idx64, cnt64
 
     flop_dense = dense_flop(w.seqlens, w.num_q_heads)
     pairs = bsa_pairs(idx, cnt, p)
@@ -287,6 +293,9 @@ def run_main(args):
         "speedup_vs_dense": t_dense / t_stem,
         "bsa_speedup_vs_dense": t_dense / timer.mean("bsa"),
         "skip_overhead": timer.mean("bsa") / (rho * t_dense) - 1.0,
+        "tile_64x128": {"kernel": "attn_bf16_kernel<sparse, 64-query rows>", "bsa_ms": dtimer.mean("q64"),
+                        "vs_128x128": dtimer.mean("q64") / timer.mean("bsa"),
+                        "tflops": bsa_flop / (dtimer.mean("q64") * 1e-3) / 1e12},
         "score_mfma_tflops": score_flop / (timer.mean("score") * 1e-3) / 1e12,
         "schedule_gbs": topk_bytes / (timer.mean("schedule") * 1e-3) / 1e9,
         "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<sparse>",
@@ -296,7 +305,8 @@ def run_main(args):
                      "algorithmic_flop_per_launch": bsa_flop},
     }
     log(f"[bench] stem {t_stem:.2f} ms (score {timer.mean('score'):.2f}, schedule "
-        f"{timer.mean('schedule'):.3f}, bsa {timer.mean('bsa'):.2f}); dense {t_dense:.2f} ms")
+        f"{timer.mean('schedule'):.3f}, bsa {timer.mean('bsa'):.2f}); dense {t_dense:.2f} ms; "
+        f"64x128 tiles {dtimer.mean('q64'):.2f} ms")
 
     if not args.no_sweep:
         res["density_sweep"] = density_sweep(args, torch, stem, S, dev)

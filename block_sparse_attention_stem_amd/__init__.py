@@ -38,7 +38,7 @@ DEFAULTS = dict(block_size=128, stride=8, chunk_size=2048, norm=1.0,
 EXPORTED = ("stem_status_string", "stem_score_workspace_bytes", "stem_score",
             "stem_schedule_topk", "stem_tpd_budget", "stem_kept_count", "stem_max_kept",
             "stem_attn_workspace_bytes", "stem_bsa_prefill", "stem_dense_prefill",
-            "stem_bsa_prefill_paged")
+            "stem_bsa_prefill_paged", "stem_bsa_prefill_q64")
 
 
 class StemError(RuntimeError):
@@ -92,6 +92,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.stem_bsa_prefill_paged.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, i32, f32, vp, vp,
                                            vp, sz, vp]
     lib.stem_bsa_prefill_paged.restype = ctypes.c_int
+    lib.stem_bsa_prefill_q64.argtypes = [P, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]
+    lib.stem_bsa_prefill_q64.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -260,6 +262,35 @@ def stem_bsa_prefill(p: Problem, q, k, v, block_idx, block_cnt, softmax_scale: O
                               _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                               _stream(stream))
     _check("stem_bsa_prefill", st)
+    return (out, lse) if lse is not None else out
+
+
+def stem_bsa_prefill_q64(p: Problem, q, k, v, block_idx, block_cnt, softmax_scale: Optional[float] = None,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         want_lse: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
+    """bf16 block-sparse attention over 64-query rows: block_idx int32 [Hq][2R][k_cap],
+    block_cnt int32 [Hq][2R]; list row 2r + s covers queries [64 s, 64 s + 64) of block row r."""
+    lib = load_library()
+    if q.dtype != torch.bfloat16:
+        raise ValueError("stem_bsa_prefill_q64: bf16 inputs only")
+    dt, _ = _attn_inputs(p, q, k, v, None)
+    _need(block_cnt, "block_cnt", torch.int32, (p.Hq, 2 * p.R))
+    if block_idx.dtype != torch.int32 or block_idx.dim() != 3 or tuple(block_idx.shape[:2]) != (p.Hq, 2 * p.R) \
+            or not block_idx.is_contiguous():
+        raise ValueError("block_idx: expected contiguous int32 [Hq][2R][k_cap]")
+    scale = 1.0 / math.sqrt(p.d) if softmax_scale is None else float(softmax_scale)
+    if out is None:
+        out = torch.empty((p.T, p.Hq, p.d), dtype=torch.bfloat16, device=q.device)
+    _need(out, "out", torch.bfloat16, (p.T, p.Hq, p.d))
+    if want_lse and lse is None:
+        lse = torch.empty((p.Hq, p.T), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, "lse", torch.float32, (p.Hq, p.T))
+    ws = _attn_workspace(p, dt, workspace, q.device)
+    st = lib.stem_bsa_prefill_q64(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(block_cnt),
+                                  int(block_idx.shape[2]), scale, _ptr(out), _ptr(lse), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream))
+    _check("stem_bsa_prefill_q64", st)
     return (out, lse) if lse is not None else out
 
 

@@ -181,23 +181,33 @@ __global__ __launch_bounds__(256) void vprep_fp8_kernel(const uint8_t *__restric
 }
 
 // Paged: row kb_local of this launch's sequences reads its tokens from the
-// page its sequence's table names (clamped into the pool).
+// page its sequence's table names (clamped into the pool), and copies that
+// page's K and V scales to the row-indexed arrays ksr / vsr [R][Hkv], so the
+// attention kernel looks scales up by row exactly as for contiguous K/V.
 __global__ __launch_bounds__(256) void vprep_fp8_paged_kernel(const uint8_t *__restrict__ v,
                                                               uint8_t *__restrict__ img8,
                                                               uint16_t *__restrict__ img16, int Hkv, int R,
                                                               const int32_t *__restrict__ table,
-                                                              int table_stride, int num_pages, SeqTable t) {
+                                                              int table_stride, int num_pages, SeqTable t,
+                                                              const float *__restrict__ ksp,
+                                                              const float *__restrict__ vsp,
+                                                              float *__restrict__ ksr, float *__restrict__ vsr) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kBlock * (kHeadDim + 16)];
   const int kb = t.row[0] + blockIdx.x, g = blockIdx.y;
   const int z = seq_of(t.row, t.n, kb);
   int page = table[(size_t)(t.z0 + z) * table_stride + (kb - t.row[z])];
   page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+  if (threadIdx.x == 0) {
+    ksr[(size_t)kb * Hkv + g] = ksp[(size_t)page * Hkv + g];
+    vsr[(size_t)kb * Hkv + g] = vsp[(size_t)page * Hkv + g];
+  }
   vprep_fp8_block(v, (size_t)page * kBlock, kb, g, img8, img16, Hkv, R, tile);
 }
 
 // ============================================================ work decode
 struct AttnItem {
   int h, g, r, z, I;
+  int half;                      // 64-query rows: which half of block row I (0 for square rows)
 };
 
 // Items are ordered by KV group, then by row from the last (longest causal
@@ -215,6 +225,27 @@ __device__ __forceinline__ AttnItem decode_attn(const AttnLaunch &a, const SeqTa
   w.r = t.row[0] + (rows - 1 - rr);
   w.z = seq_of(t.row, t.n, w.r);
   w.I = w.r - t.row[w.z];
+  w.half = 0;
+  return w;
+}
+
+// 64-query rows: the same order over twice as many rows.  List row r64 =
+// 2 r + half covers queries [64 half, 64 half + 64) of block row r; I is the
+// block row's index in its sequence (the key block holding the diagonal).
+__device__ __forceinline__ AttnItem decode_attn_q64(const AttnLaunch &a, const SeqTable &t, int rows) {
+  const int G = a.Hq / a.Hkv;
+  const int rows64 = 2 * rows;
+  const int item = xcd_chunk_item(blockIdx.x, rows64 * a.Hq);
+  const int slot = item / G, hh = item - slot * G;
+  AttnItem w;
+  w.g = slot / rows64;
+  const int rr = slot - w.g * rows64;
+  w.h = w.g * G + hh;
+  w.r = 2 * t.row[0] + (rows64 - 1 - rr);
+  const int r128 = w.r >> 1;
+  w.z = seq_of(t.row, t.n, r128);
+  w.I = r128 - t.row[w.z];
+  w.half = w.r & 1;
   return w;
 }
 
@@ -298,14 +329,26 @@ __device__ __forceinline__ float softmax_step(f32x16 (&s)[4], bool diag, int qlo
 // O is rescaled lazily: the running max used for the weights is raised only
 // when a block's max exceeds it by more than 2^8 (weights stay <= 256, exact
 // range for fp16), which skips almost every rescale.
+//
+// kQ = 64 (64-query rows against 128-key blocks).  The same 8 waves, groups,
+// tiles and loads; a wave takes 32 queries (qw = w & 1) and one 32-key
+// sub-tile tw = (w >> 1) & 1 of its group's half, i.e. exactly the work of a
+// square-row wave restricted to one of its two key tiles: 8 S^T and 8 P.V
+// MFMAs per phase instead of 16 + 16.  The four key quarters of a query keep
+// separate online-softmax states, merged at the end.
 constexpr float kLazyLog2 = 8.f;
 constexpr int kHalfK = 64 * kRow16;              // K half: 64 keys x 17 chunks (elements)
 constexpr int kRowVh = 72;                       // V^T half row: 64 keys + pad chunk (elements)
 constexpr int kHalfV = kHeadDim * kRowVh;        // V^T half: 128 dims x 9 chunks (elements)
 constexpr uint32_t kBufWord3 = 0x00020000u;      // raw buffer descriptor word 3 (gfx9 dword access)
 
-template <bool kSparse>
+template <bool kSparse, int kQ>
 __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTable t, int rows) {
+  static_assert(kQ == 128 || kQ == 64, "query rows of 128 or 64 tokens");
+  constexpr bool kQ64 = kQ == 64;
+  constexpr int NT = kQ64 ? 1 : 2;          // 32-key S^T tiles per wave
+  constexpr int NP = 8 * NT;                // P.V MFMAs per phase
+  constexpr int NM = 16 * NT;               // MFMAs per phase (P.V + S^T)
   __shared__ __attribute__((aligned(1024))) uint16_t K0[2 * kHalfK];   // bf16 K halves, [key][d]
   __shared__ __attribute__((aligned(1024))) uint16_t V0[2 * kHalfV];   // fp16 V^T halves, [d][key]
   __shared__ __attribute__((aligned(1024))) uint16_t K1[2 * kHalfK];
@@ -314,22 +357,25 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
   const int tid = threadIdx.x, lane = tid & 63;
   const int lg = lane >> 5, l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qw = wv & 3, kh = wv >> 2;
-  const AttnItem w = decode_attn(a, t, rows);
+  const int wg = wv & 3, kh = wv >> 2;      // wg: the wave's share of its group's loads
+  const int qw = kQ64 ? (wv & 1) : wg;      // 32-query slice
+  const int tw = kQ64 ? ((wv >> 1) & 1) : 0;
+  const AttnItem w = kQ64 ? decode_attn_q64(a, t, rows) : decode_attn(a, t, rows);
   const int zrow = t.row[w.z];
   const size_t ztok = (size_t)t.tok[w.z];
   const size_t qtok0 = ztok + (size_t)w.I * kBlock;
-  const int qloc = qw * 32 + l32;
+  const int qloc = 64 * w.half + qw * 32 + l32;   // query offset in the diagonal block
   const size_t qtok = qtok0 + qloc;
-  cint32 *list = kSparse ? as_const(a.idx) + ((size_t)w.h * a.R + w.r) * a.k_cap : nullptr;
+  const size_t list_rows = kQ64 ? 2 * (size_t)a.R : (size_t)a.R;
+  cint32 *list = kSparse ? as_const(a.idx) + ((size_t)w.h * list_rows + w.r) * a.k_cap : nullptr;
   // Lists are trusted to be ascending in [0, I]; counts and ids are still
   // clamped so a malformed list can never address outside the sequence.
-  int n_blk = kSparse ? as_const(a.cnt)[(size_t)w.h * a.R + w.r] : w.I + 1;
+  int n_blk = kSparse ? as_const(a.cnt)[(size_t)w.h * list_rows + w.r] : w.I + 1;
   if (kSparse && n_blk > a.k_cap) n_blk = a.k_cap;
   __bf16 *orow = (__bf16 *)a.out + (qtok * a.Hq + w.h) * kHeadDim;
   float *lse = a.lse ? a.lse + (size_t)w.h * a.T + qtok : nullptr;
   if (n_blk <= 0) {
-    if (kh == 0) write_empty(orow, lse, lg);
+    if (kh == 0 && (!kQ64 || tw == 0)) write_empty(orow, lse, lg);   // the waves that hold results
     return;
   }
   auto blk = [&](int b) { return kSparse ? (int)(list[b] < 0 ? 0 : (list[b] > w.I ? w.I : list[b])) : b; };
@@ -350,14 +396,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
   //   V half: 18 loads; slot s -> dim row s / 9, chunk s % 9 of this half's
   //           8 image chunks (chunk 8 is the pad and re-reads chunk 0).
   const uint32_t kstride_b = (uint32_t)a.Hkv * kHeadDim * 2;
-  const int nkk = qw == 0 ? 5 : 4, nkv = qw < 2 ? 5 : 4;
+  const int nkk = wg == 0 ? 5 : 4, nkv = wg < 2 ? 5 : 4;
   uint32_t koff[5], voff[5];
 #pragma unroll
   for (int m = 0; m < 5; ++m) {
-    const int sk = 64 * (qw + 4 * m) + lane;
+    const int sk = 64 * (wg + 4 * m) + lane;
     const int rk = sk / 17, ck = sk - 17 * rk;
     koff[m] = (uint32_t)rk * kstride_b + 16 * (ck < 16 ? ck : 0);
-    const int sv = 64 * (qw + 4 * m) + lane;
+    const int sv = 64 * (wg + 4 * m) + lane;
     const int rv = sv / 9, cv = sv - 9 * rv;
     voff[m] = (uint32_t)(rv * kRow16 * 2 + 16 * (8 * kh + (cv < 8 ? cv : 0)));
   }
@@ -371,7 +417,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
     uint16_t *d = Kd + kh * kHalfK;
 #pragma unroll
     for (int m = 0; m < 5; ++m)
-      if (m < nkk) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(d + (qw + 4 * m) * 512), 16, koff[m], 0, 0, 0);
+      if (m < nkk) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(d + (wg + 4 * m) * 512), 16, koff[m], 0, 0, 0);
   };
   // The loads of one block step: d = 0..4 are K loads m = d of the next
   // block (a descriptor of size 0 when there is none: no memory is read and
@@ -392,8 +438,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
   f32x16 o[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) o[u] = f32x16{};
-  f32x16 s[2];            // S^T of the current block (this wave's 64 keys)
-  u32x4 pk[4];            // P of the previous block, fp16, one 16-key step each
+  f32x16 s[NT];           // S^T of the current block (this wave's 64 or 32 keys)
+  u32x4 pk[2 * NT];       // P of the previous block, fp16, one 16-key step each
 
   // MFMA phase: P.V of the previous block (if kPV) from the V^T half in Vp,
   // then S^T of this block from the K half in Kc, as one stream of MFMAs
@@ -410,31 +456,40 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
     uint16_t *dk = Kn + kh * kHalfK, *dv = Vc + kh * kHalfV;
     auto dma = [&](int d) __attribute__((always_inline)) {
       if (d < 5) {
-        if (d < nkk) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_ptr(dk + (qw + 4 * d) * 512), 16, koff[d], 0, 0, 0);
+        if (d < nkk) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_ptr(dk + (wg + 4 * d) * 512), 16, koff[d], 0, 0, 0);
       } else {
         const int m = d - 5;
-        if (m < nkv) __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_ptr(dv + (qw + 4 * m) * 512), 16, voff[m], 0, 0, 0);
+        if (m < nkv) __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_ptr(dv + (wg + 4 * m) * 512), 16, voff[m], 0, 0, 0);
       }
     };
-    constexpr int i0 = PV ? 0 : 16;
-    const uint16_t *vad = Vp + kh * kHalfV + l32 * kRowVh + 8 * lg;
-    const uint16_t *kad = Kc + kh * kHalfK + l32 * kRow16 + 8 * lg;
+    constexpr int i0 = PV ? 0 : NP;
+    // kQ = 64: the wave's key tile tw is 32 K rows further and two 16-key
+    // steps further along the V^T rows
+    const uint16_t *vad = Vp + kh * kHalfV + l32 * kRowVh + 8 * lg + 32 * tw;
+    const uint16_t *kad = Kc + kh * kHalfK + l32 * kRow16 + 8 * lg + 32 * kRow16 * tw;
     auto rd = [&](int i) __attribute__((always_inline)) {
-      return i < 16 ? ld16(vad + 32 * kRowVh * (i & 3) + 16 * (i >> 2))
-                    : ld16(kad + 32 * kRow16 * ((i - 16) & 1) + 16 * ((i - 16) >> 1));
+      return i < NP ? ld16(vad + 32 * kRowVh * (i & 3) + 16 * (i >> 2))
+                    : ld16(kad + 32 * kRow16 * ((i - NP) % NT) + 16 * ((i - NP) / NT));
     };
-    u32x4 r[32];
+    u32x4 r[NM];
 #pragma unroll
     for (int i = i0; i < i0 + kAhead; ++i) r[i] = rd(i);
 #pragma unroll
-    for (int i = i0; i < 32; ++i) {
-      if (i + kAhead < 32) r[i + kAhead] = rd(i + kAhead);
-      if (PV ? (i % 3 == 1 && i < 30) : (i - 16 < 10)) dma(PV ? i / 3 : i - 16);
+    for (int i = i0; i < NM; ++i) {
+      if (i + kAhead < NM) r[i + kAhead] = rd(i + kAhead);
+      if constexpr (!kQ64) {
+        if (PV ? (i % 3 == 1 && i < 30) : (i - 16 < 10)) dma(PV ? i / 3 : i - 16);
+      } else if (PV) {
+        if (i < 10) dma(i);                  // 10 loads over 16 MFMAs
+      } else if (i - NP < 5) {
+        dma(2 * (i - NP));                   // 10 loads over 8 MFMAs
+        dma(2 * (i - NP) + 1);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      if (i < 16) {
+      if (i < NP) {
         o[i & 3] = mfma_f16_32x32x16(as_f16x8(r[i]), as_f16x8(pk[i >> 2]), o[i & 3]);
       } else {
-        const int tt = (i - 16) & 1, ks = (i - 16) >> 1;
+        const int tt = (i - NP) % NT, ks = (i - NP) / NT;
         s[tt] = mfma_bf16_32x32x16(as_bf16x8(r[i]), qf[ks], ks == 0 ? f32x16{} : s[tt]);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -442,13 +497,13 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
   };
   // P.V of the last block (no S^T after it).
   auto pv_last = [&](const uint16_t *Vp) __attribute__((always_inline)) {
-    const uint16_t *vad = Vp + kh * kHalfV + l32 * kRowVh + 8 * lg;
-    u32x4 r[16];
+    const uint16_t *vad = Vp + kh * kHalfV + l32 * kRowVh + 8 * lg + 32 * tw;
+    u32x4 r[NP];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) r[i] = ld16(vad + 32 * kRowVh * (i & 3) + 16 * (i >> 2));
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      if (i + kAhead < 16) r[i + kAhead] = ld16(vad + 32 * kRowVh * ((i + kAhead) & 3) + 16 * ((i + kAhead) >> 2));
+    for (int i = 0; i < NP; ++i) {
+      if (i + kAhead < NP) r[i + kAhead] = ld16(vad + 32 * kRowVh * ((i + kAhead) & 3) + 16 * ((i + kAhead) >> 2));
       __builtin_amdgcn_sched_barrier(0);
       o[i & 3] = mfma_f16_32x32x16(as_f16x8(r[i]), as_f16x8(pk[i >> 2]), o[i & 3]);
       __builtin_amdgcn_sched_barrier(0);
@@ -461,16 +516,16 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
   // the exponent offset is 0, so every weight is 0.
   auto softmax = [&](bool diag) __attribute__((always_inline)) {
     if (diag) {
-      const int lim = qloc - 64 * kh - 4 * lg;        // key > qloc  <=>  local key offset > lim
+      const int lim = qloc - 64 * kh - 32 * tw - 4 * lg;   // key > qloc  <=>  local key offset > lim
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           s[tt][i] = (32 * tt + 8 * (i >> 2) + (i & 3) > lim) ? -INFINITY : s[tt][i];
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[tt][i]);
     mx = wave_max_xor32(mx) * c;
@@ -487,7 +542,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
+    for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         s[tt][i] = __builtin_amdgcn_exp2f(fmaf(s[tt][i], c, -m_use));
@@ -495,7 +550,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
       }
     l_run += psum;
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
+    for (int cc = 0; cc < 2 * NT; ++cc) {
       const int tt = cc >> 1, j0 = 8 * (cc & 1);
       pk[cc] = u32x4{pack_f16x2(s[tt][j0 + 0], s[tt][j0 + 1]), pack_f16x2(s[tt][j0 + 2], s[tt][j0 + 3]),
                      pack_f16x2(s[tt][j0 + 4], s[tt][j0 + 5]), pack_f16x2(s[tt][j0 + 6], s[tt][j0 + 7])};
@@ -534,6 +589,48 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
   pv_last((n_blk & 1) ? V0 : V1);
   if (kh == 0) block_sync();         // realign the groups
 
+  if constexpr (kQ64) {
+    // merge the four key quarters kq = 2 kh + tw of each query slice: waves
+    // with kq = 1..3 hand (O, m, l) to the kq = 0 wave through LDS (six
+    // 66 x 64-float buffers, two per K/V array)
+    block_sync();
+    auto xbuf = [&](int j) __attribute__((always_inline)) {       // j = 3 qw + kq - 1
+      float *base = (float *)(j < 2 ? K0 : (j < 4 ? V0 : K1));
+      return base + (j & 1) * (66 * 64);
+    };
+    const int kq = 2 * kh + tw;
+    if (kq != 0) {
+      float *xch = xbuf(3 * qw + kq - 1);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xch[(16 * u + i) * 64 + lane] = o[u][i];
+      xch[64 * 64 + lane] = m_run;
+      xch[65 * 64 + lane] = l_run;
+    }
+    block_sync();
+    if (kq == 0) {
+      const float *x1 = xbuf(3 * qw), *x2 = xbuf(3 * qw + 1), *x3 = xbuf(3 * qw + 2);
+      const float m1 = x1[64 * 64 + lane], m2 = x2[64 * 64 + lane], m3 = x3[64 * 64 + lane];
+      // finite: the query's own key, or every key of an earlier listed block, is visible
+      const float m = fmaxf(fmaxf(m_run, m1), fmaxf(m2, m3));
+      auto wgt = [&](float mi) { return mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - m); };
+      const float a0 = wgt(m_run), a1 = wgt(m1), a2 = wgt(m2), a3 = wgt(m3);
+      float l = l_run * a0 + x1[65 * 64 + lane] * a1 + x2[65 * 64 + lane] * a2 + x3[65 * 64 + lane] * a3;
+      l += __shfl_xor(l, 32, 64);
+      const float inv = 1.f / l;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int e = (16 * u + i) * 64 + lane;
+          o[u][i] = (o[u][i] * a0 + x1[e] * a1 + x2[e] * a2 + x3[e] * a3) * inv;
+        }
+      write_out(orow, o, 1.f, lg);
+      if (lse && lg == 0) *lse = (m + __log2f(l)) * 0.69314718055994531f;
+    }
+    return;
+  }
   // merge the two key halves: waves 4-7 hand (O, m, l) to waves 0-3 through LDS
   block_sync();
   float *xch = (float *)(qw < 2 ? K0 : K1) + (qw & 1) * (66 * 64);
@@ -605,8 +702,9 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
     return;
   }
   auto clampJ = [&](int x) { return x < 0 ? 0 : (x > w.I ? w.I : x); };
-  // Key-block row of block J in K, V and their scales: its page when K/V
-  // are paged (clamped into the pool), else its packed row.
+  // Where K of block J starts: its page when K/V are paged (clamped into the
+  // pool), else its packed row.  Scales are always indexed by row: for paged
+  // K/V the pre-pass copies each page's scales to row-indexed arrays.
   cint32 *ptab = a.table ? as_const(a.table) + (size_t)(t.z0 + w.z) * a.table_stride : nullptr;
   auto srow = [&](int J) {
     if (!ptab) return zrow + J;
@@ -683,7 +781,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
     if (v16_pending) wait_vmcnt<8>(); else wait_vmcnt<4>();
     block_sync();
     const bool diag = may_diag && (J == w.I);
-    const int sr = srow(J);
+    const int sr = zrow + J;
     const float c = cq * a.k_scale[(size_t)sr * a.Hkv + w.g];
     const float vs = a.v_scale[(size_t)sr * a.Hkv + w.g];
     f32x16 s[4];
@@ -774,10 +872,13 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
 
 // ================================================================ launchers
 size_t attn_workspace_bytes(int Hkv, int R, bool fp8) {
-  const size_t per_block = fp8 ? (size_t)kTile8 + 2 * (size_t)kTile16 : 2 * (size_t)kTile16;
-  return (size_t)Hkv * R * per_block;
+  if (!fp8) return (size_t)Hkv * R * 2 * (size_t)kTile16;
+  return attn_workspace_scales_offset(Hkv, R) + 2 * (size_t)Hkv * R * sizeof(float);
 }
 size_t attn_workspace_img16_offset(int Hkv, int R) { return (size_t)Hkv * R * kTile8; }
+size_t attn_workspace_scales_offset(int Hkv, int R) {
+  return (size_t)Hkv * R * ((size_t)kTile8 + 2 * (size_t)kTile16);
+}
 
 hipError_t launch_vprep(const AttnLaunch &a, bool fp8, hipStream_t s) {
   const dim3 grid(a.R, a.Hkv);
@@ -792,7 +893,8 @@ hipError_t launch_vprep(const AttnLaunch &a, bool fp8, hipStream_t s) {
 hipError_t launch_vprep_paged(const AttnLaunch &a, const SeqTable &t, int rows, hipStream_t s) {
   const dim3 grid(rows, a.Hkv);
   hipLaunchKernelGGL(vprep_fp8_paged_kernel, grid, dim3(256), 0, s, (const uint8_t *)a.v, a.vimg8, a.vimg16, a.Hkv,
-                     a.R, a.table, a.table_stride, a.num_pages, t);
+                     a.R, a.table, a.table_stride, a.num_pages, t, a.k_scale_pages, a.v_scale_pages,
+                     (float *)a.k_scale, (float *)a.v_scale);
   return hipGetLastError();
 }
 
@@ -803,9 +905,15 @@ hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows, bool sp
     if (sparse) hipLaunchKernelGGL(attn_fp8_kernel<true>, grid, dim3(256), 0, s, a, t, rows);
     else hipLaunchKernelGGL(attn_fp8_kernel<false>, grid, dim3(256), 0, s, a, t, rows);
   } else {
-    if (sparse) hipLaunchKernelGGL(attn_bf16_kernel<true>, grid, dim3(512), 0, s, a, t, rows);
-    else hipLaunchKernelGGL(attn_bf16_kernel<false>, grid, dim3(512), 0, s, a, t, rows);
+    if (sparse) hipLaunchKernelGGL((attn_bf16_kernel<true, 128>), grid, dim3(512), 0, s, a, t, rows);
+    else hipLaunchKernelGGL((attn_bf16_kernel<false, 128>), grid, dim3(512), 0, s, a, t, rows);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_q64(const AttnLaunch &a, const SeqTable &t, int rows, hipStream_t s) {
+  const dim3 grid(2 * rows * a.Hq);
+  hipLaunchKernelGGL((attn_bf16_kernel<true, 64>), grid, dim3(512), 0, s, a, t, rows);
   return hipGetLastError();
 }
 

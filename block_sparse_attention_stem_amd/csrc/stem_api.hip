@@ -214,7 +214,8 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
                        const float *v_scale, const int32_t *block_idx, const int32_t *block_cnt,
                        int32_t k_cap, float softmax_scale, void *out, float *lse, void *workspace,
                        size_t workspace_bytes, void *stream, bool sparse,
-                       const int32_t *table = nullptr, int32_t table_stride = 0, int32_t num_pages = 0) {
+                       const int32_t *table = nullptr, int32_t table_stride = 0, int32_t num_pages = 0,
+                       bool q64 = false) {
   Shape s;
   int st = check_problem(p, &s);
   if (st != STEM_OK) return st;
@@ -261,6 +262,16 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
   a.table = table;
   a.table_stride = table_stride;
   a.num_pages = num_pages;
+  a.k_scale_pages = nullptr;
+  a.v_scale_pages = nullptr;
+  if (table) {
+    // the paged pre-pass copies page scales to row-indexed arrays
+    float *rs = (float *)((uint8_t *)workspace + attn_workspace_scales_offset(s.Hkv, s.R));
+    a.k_scale_pages = k_scale;
+    a.v_scale_pages = v_scale;
+    a.k_scale = rs;
+    a.v_scale = rs + (size_t)s.R * s.Hkv;
+  }
   hipStream_t hs = as_stream(stream);
   if (!table && launch_vprep(a, fp8, hs) != hipSuccess) return STEM_ERR_HIP;
   for (int z0 = 0; z0 < s.B; z0 += kMaxSeqsPerLaunch) {
@@ -268,9 +279,10 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
     SeqTable t;
     fill_table(p, z0, n, &t);
     const int rows = t.row[n] - t.row[0];
-    if ((int64_t)rows * s.Hq >= ((int64_t)1 << 31)) return STEM_ERR_UNSUPPORTED;
+    if ((int64_t)rows * s.Hq * (q64 ? 2 : 1) >= ((int64_t)1 << 31)) return STEM_ERR_UNSUPPORTED;
     if (table && launch_vprep_paged(a, t, rows, hs) != hipSuccess) return STEM_ERR_HIP;
-    if (launch_attn(a, t, rows, sparse, fp8, hs) != hipSuccess) return STEM_ERR_HIP;
+    const hipError_t e = q64 ? launch_attn_q64(a, t, rows, hs) : launch_attn(a, t, rows, sparse, fp8, hs);
+    if (e != hipSuccess) return STEM_ERR_HIP;
   }
   return STEM_OK;
 }
@@ -290,6 +302,14 @@ int stem_dense_prefill(const stem_problem_t *p, int32_t dtype, const void *q, co
                        void *workspace, size_t workspace_bytes, void *stream) {
   return attn_common(p, dtype, q, k, v, q_scale, k_scale, v_scale, nullptr, nullptr, 0,
                      softmax_scale, out, lse, workspace, workspace_bytes, stream, false);
+}
+
+int stem_bsa_prefill_q64(const stem_problem_t *p, const void *q, const void *k, const void *v,
+                         const int32_t *block_idx, const int32_t *block_cnt, int32_t k_cap,
+                         float softmax_scale, void *out, float *lse, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  return attn_common(p, STEM_DTYPE_BF16, q, k, v, nullptr, nullptr, nullptr, block_idx, block_cnt, k_cap,
+                     softmax_scale, out, lse, workspace, workspace_bytes, stream, true, nullptr, 0, 0, true);
 }
 
 int stem_bsa_prefill_paged(const stem_problem_t *p, const void *q, const void *k_pages,

@@ -138,16 +138,24 @@ struct AttnLaunch {
   // Paged K/V (fp8 only; null table = contiguous varlen tensors): k and v
   // point at pools of num_pages pages of kBlock tokens, [page][token][Hkv][d];
   // table[z * table_stride + J] is the page of key block J of sequence z;
-  // k_scale / v_scale are then [page][Hkv].
+  // the caller's scales k_scale_pages / v_scale_pages are [page][Hkv], and
+  // k_scale / v_scale then point at row-indexed copies in the workspace
+  // that the paged pre-pass fills.
   const int32_t *table;
   int32_t table_stride, num_pages;
+  const float *k_scale_pages, *v_scale_pages;
 };
+// fp8 workspace: e4m3 V^T images, then fp16 ones, then K and V scales [R][Hkv]
+// (row-indexed copies, written by the paged pre-pass only).
 size_t attn_workspace_bytes(int Hkv, int R, bool fp8);
 size_t attn_workspace_img16_offset(int Hkv, int R);
+size_t attn_workspace_scales_offset(int Hkv, int R);
 hipError_t launch_vprep(const AttnLaunch &a, bool fp8, hipStream_t s);
 // Paged pre-pass for the rows of one launch's sequences.
 hipError_t launch_vprep_paged(const AttnLaunch &a, const SeqTable &t, int rows_in_launch, hipStream_t s);
 hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows_in_launch,
                        bool sparse, bool fp8, hipStream_t s);
+// bf16 block-sparse attention over 64-query rows (lists [Hq][2R][k_cap]).
+hipError_t launch_attn_q64(const AttnLaunch &a, const SeqTable &t, int rows_in_launch, hipStream_t s);
 
 }  // namespace stem

@@ -143,9 +143,11 @@ int32_t stem_max_kept(const stem_problem_t *p, const double *k_start_host, doubl
  * dtype).  Each call first rewrites it with V in the tile layout the
  * attention kernel loads (per KV head and key block, the 128 x 128 V^T tile
  * with one 16-byte pad chunk per row; fp16 for bf16 inputs, e4m3 plus fp16
- * for fp8 inputs): T * Hkv * 272 bytes for bf16, T * Hkv * 416 bytes for
- * fp8 (d = 128).  Contents on return are unspecified; concurrent calls need
- * separate workspaces.
+ * for fp8 inputs): T * Hkv * 272 bytes for bf16; for fp8, T * Hkv * 416
+ * bytes plus 8 bytes per (key block, KV head) for the row-indexed K and V
+ * scales that stem_bsa_prefill_paged gathers from its pages (d = 128).
+ * Contents on return are unspecified; concurrent calls need separate
+ * workspaces.
  * ------------------------------------------------------------------------- */
 size_t stem_attn_workspace_bytes(const stem_problem_t *p, int32_t dtype);
 
@@ -211,6 +213,27 @@ int stem_bsa_prefill_paged(const stem_problem_t *p, const void *q, const void *k
                            int32_t table_stride, int32_t num_pages, const int32_t *block_idx,
                            const int32_t *block_cnt, int32_t k_cap, float softmax_scale, void *out,
                            float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------------------
+ * Block-sparse attention with 64-query rows against 128-key blocks (bf16).
+ * The youleyou HPC-BSA article §三.3.1 names 64 x 128 blocks next to
+ * 128 x 128; this entry point takes lists over query blocks of 64 tokens:
+ * list row 2 r + s (s = 0, 1) covers queries [64 s, 64 s + 64) of block row
+ * r (r as in stem_bsa_prefill), and its entries are 128-token key-block ids
+ * J (local to the sequence), ascending, in [0, I] with I the row's block
+ * index; keys later than the query are masked as in stem_bsa_prefill.
+ * block_idx: int32 [Hq][2 R][k_cap]; block_cnt: int32 [Hq][2 R].
+ * q, k, v: bf16 as in stem_bsa_prefill; out, lse, softmax_scale, workspace
+ *   (stem_attn_workspace_bytes(p, BF16)) likewise.  Precision as the bf16
+ *   path of stem_bsa_prefill.
+ * Giving both halves of a row the row's list reproduces stem_bsa_prefill up
+ * to fp32 summation order.
+ * Errors: as stem_bsa_prefill with dtype BF16.
+ * ------------------------------------------------------------------------- */
+int stem_bsa_prefill_q64(const stem_problem_t *p, const void *q, const void *k, const void *v,
+                         const int32_t *block_idx, const int32_t *block_cnt, int32_t k_cap,
+                         float softmax_scale, void *out, float *lse, void *workspace,
+                         size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

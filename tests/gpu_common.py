@@ -131,3 +131,25 @@ def page_pool(k8, v8, ks, vs, seqlens, spare=7, seed=0):
         table[z, :nb] = perm[r:r + nb].to(torch.int32)
         r += nb
     return kp, vp, ksp, vsp, table
+
+
+def random_q64_lists(seqlens, Hq, seed=0, p_empty=0.1, spare=2):
+    """Random lists for 64-query rows (row 2r + s of a sequence lists
+    128-token key blocks in [0, r]): ascending, random sizes, about p_empty
+    of the rows empty and many without the diagonal block; -1 padded to the
+    longest list plus `spare`.  Returns (idx [Hq][R64][k_cap], cnt [Hq][R64]) int32."""
+    rng = np.random.default_rng(seed)
+    rows = []                                   # diagonal block of every 64-query row
+    for L in seqlens:
+        rows += [r64 // 2 for r64 in range(int(L) // 64)]
+    k_cap = max(rows) + 1 + spare
+    idx = np.full((Hq, len(rows), k_cap), -1, np.int32)
+    cnt = np.zeros((Hq, len(rows)), np.int32)
+    for h in range(Hq):
+        for i, top in enumerate(rows):
+            if rng.random() < p_empty:
+                continue
+            sel = np.sort(rng.choice(top + 1, size=int(rng.integers(1, top + 2)), replace=False))
+            idx[h, i, :sel.size] = sel
+            cnt[h, i] = sel.size
+    return idx, cnt

@@ -136,7 +136,7 @@ def test_attention_argument_errors():
     assert lib.stem_dense_prefill(p.ref, 0, f, f, f, None, None, None, 0.1, f, None, ctypes.c_void_p(0x1010),
                                   W, None) == 4
     assert stem.stem_attn_workspace_bytes(p, 0) == 1024 * 2 * 272
-    assert stem.stem_attn_workspace_bytes(p, 1) == 1024 * 2 * 416
+    assert stem.stem_attn_workspace_bytes(p, 1) == 1024 * 2 * 416 + (1024 // 128) * 2 * 8
     assert stem.stem_attn_workspace_bytes(p, 5) == 0
 
 
@@ -158,6 +158,21 @@ def test_paged_attention_argument_errors():
     # a ragged sequence length is reported before anything else
     bad = stem.Problem([0, 1000], 4, 2)
     assert call(bad.ref, f, f, f, f, f, f, f, 8, 16, f, f, 8, 0.1, f, None, f, W, None) == 2
+
+
+def test_q64_attention_argument_errors():
+    """Every call below carries one invalid argument, so nothing is launched."""
+    lib = stem.load_library()
+    p = stem.Problem([0, 1024], 4, 2)
+    f = FAKE
+    W = 1 << 30
+    call = lib.stem_bsa_prefill_q64
+    assert call(p.ref, None, f, f, f, f, 8, 0.1, f, None, f, W, None) == 1        # null q
+    assert call(p.ref, f, f, f, None, f, 8, 0.1, f, None, f, W, None) == 1        # null lists
+    assert call(p.ref, f, f, f, f, f, 0, 0.1, f, None, f, W, None) == 1           # k_cap 0
+    assert call(p.ref, f, f, f, f, f, 8, -1.0, f, None, f, W, None) == 1          # scale
+    assert call(p.ref, f, f, f, f, f, 8, 0.1, f, None, f, 100, None) == 4         # workspace size
+    assert call(stem.Problem([0, 1000], 4, 2).ref, f, f, f, f, f, 8, 0.1, f, None, f, W, None) == 2
 
 
 def test_package_defaults_match_the_doc_table():

@@ -101,6 +101,13 @@ def _run(w, fp8):
         paged_equal = bool(torch.equal(pout, out)) and bool(torch.equal(plse, lse))
         note(f"[{w.name}] paged ({kp.shape[0]} pages) equals contiguous: {paged_equal}")
         del kpd, vpd, tabd, pout, plse
+    out64 = lse64 = None
+    if not fp8:
+        # 64-query rows, each half given its 128-query row's list
+        out64, lse64 = torch.empty_like(out), torch.empty_like(lse)
+        stem.stem_bsa_prefill_q64(p, qa, ka, va, idx.repeat_interleave(2, dim=1).contiguous(),
+                                  cnt.repeat_interleave(2, dim=1).contiguous(), SCALE, out=out64, lse=lse64,
+                                  workspace=aws)
     stem.stem_dense_prefill(p, qa, ka, va, SCALE, scales=scales, out=dout, workspace=aws)
     torch.cuda.synchronize()
     rows = _sample_rows(w)
@@ -109,6 +116,11 @@ def _run(w, fp8):
                out=_gather_rows(out, rows), dout=_gather_rows(dout, rows),
                lse={(hi, r): lse[h, r * 128:(r + 1) * 128].to(torch.float64).cpu().numpy()
                     for hi, h in enumerate(HS) for r in rows})
+    if out64 is not None:
+        res["out64"] = _gather_rows(out64, rows)
+        res["lse64"] = {(hi, r): lse64[h, r * 128:(r + 1) * 128].to(torch.float64).cpu().numpy()
+                        for hi, h in enumerate(HS) for r in rows}
+        del out64, lse64
     del qd, kd, vd, out, dout, lse, scores, idx, cnt, aws, ws
     torch.cuda.empty_cache()
     bf = _subset64(q, k, v)
@@ -164,6 +176,20 @@ def test_block_sparse_attention_on_sampled_rows(big):
                                       SCALE, rows=pairs)
     bar = (FP8_MAX_ABS, None) if fp8 else (BF16_MAX_ABS, BF16_MEAN_REL)
     _compare_rows(big, ro, rl, big["out"], big["lse"], bar, f"{w.name} bsa {len(pairs)} rows")
+
+
+def test_q64_rows_on_sampled_rows(big):
+    """The 64 x 128 variant with each half given its row's list: the same
+    oracle result as the square rows (a pinned identity of the oracle)."""
+    if "out64" not in big:
+        pytest.skip("fp8 layer: the 64-query variant is bf16 only")
+    w = big["w"]
+    qs, ks, vs = big["attn_ref_inputs"]
+    pairs = [(hi, r) for hi in range(len(HS)) for r in big["rows"]]
+    ro, rl = O.block_sparse_attention(qs, ks, vs, big["idx"][HS], big["cnt"][HS], w.cu_seqlens, len(HS),
+                                      len(KS), SCALE, rows=pairs)
+    _compare_rows(big, ro, rl, big["out64"], big["lse64"], (BF16_MAX_ABS, BF16_MEAN_REL),
+                  f"{w.name} q64 {len(pairs)} rows")
 
 
 def test_dense_attention_on_sampled_rows(big):

@@ -16,7 +16,7 @@ import oracle as O
 import stem_synth as S
 from gpu_common import (BF16_MAX_ABS, BF16_MEAN_REL, FP8_MAX_ABS, check_lse, check_out,
                         check_scores, dequant, dev, f64, lists_equal, make_inputs, note,
-                        page_pool, quantize_fp8, to_dev)
+                        page_pool, quantize_fp8, random_q64_lists, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -337,3 +337,55 @@ def test_fp8_paged_matches_oracle_and_contiguous(fp8_small):
                                        SCALE, scales=sc_paged)
     do, _ = O.dense_causal_attention(qf, kf, vf, cu, 4, 2, SCALE)
     check_out(f64(fout), do, FP8_MAX_ABS, None, "fp8 paged all blocks")
+
+
+# ------------------------------------------------ 64-query rows (64 x 128) ---
+
+def test_q64_random_lists_match_oracle(varlen):
+    """Rows of 64 queries against 128-key blocks, each row with its own random
+    list (empty rows, rows without the diagonal block), vs the oracle."""
+    lens, (q, k, v), (qf, kf, vf) = varlen
+    cu = S.cu_from_lengths(lens)
+    p = stem.Problem(cu, 4, 2)
+    qd, kd, vd = to_dev(q, k, v)
+    ri, rc = random_q64_lists(lens, 4, seed=31)
+    assert (rc == 0).any() and ri.shape[1] == 2 * p.R
+    out, lse = stem.stem_bsa_prefill_q64(p, qd, kd, vd, torch.from_numpy(ri).to(dev()),
+                                         torch.from_numpy(rc).to(dev()), SCALE, want_lse=True)
+    ro, rl = O.block_sparse_attention(qf, kf, vf, ri, rc, cu, 4, 2, SCALE, q_block=64)
+    check_out(f64(out), ro, BF16_MAX_ABS, BF16_MEAN_REL, "q64 random lists")
+    check_lse(lse.cpu().numpy().astype(np.float64), rl, "q64 random lists")
+
+
+def test_q64_parent_lists_match_square_rows(varlen):
+    """Both 64-query halves given the Stem list of their 128-query row: the
+    oracle's square-row result, and the square-row kernel's within the bar."""
+    lens, (q, k, v), (qf, kf, vf) = varlen
+    cu = S.cu_from_lengths(lens)
+    p = stem.Problem(cu, 4, 2)
+    qd, kd, vd = to_dev(q, k, v)
+    ref = _oracle_scores(qf, kf, vf, cu, 4, 2, 0.2)
+    ks = [2, 4, 1, 5]
+    kcap = stem.stem_max_kept(p, ks, 0.5, 1.0, 1, 1)
+    ri, rc = O.schedule_topk(ref, cu, ks, 0.5, 1.0, 1, 1, kcap)
+    idx64 = torch.from_numpy(np.repeat(ri, 2, axis=1)).to(dev())
+    cnt64 = torch.from_numpy(np.repeat(rc, 2, axis=1)).to(dev())
+    out, lse = stem.stem_bsa_prefill_q64(p, qd, kd, vd, idx64, cnt64, SCALE, want_lse=True)
+    ro, rl = O.block_sparse_attention(qf, kf, vf, ri, rc, cu, 4, 2, SCALE)
+    check_out(f64(out), ro, BF16_MAX_ABS, BF16_MEAN_REL, "q64 parent lists")
+    check_lse(lse.cpu().numpy().astype(np.float64), rl, "q64 parent lists")
+    sq = stem.stem_bsa_prefill(p, qd, kd, vd, torch.from_numpy(ri).to(dev()), torch.from_numpy(rc).to(dev()),
+                               SCALE)
+    check_out(f64(out), f64(sq), BF16_MAX_ABS, None, "q64 vs square-row kernel")
+
+
+def test_q64_every_block_listed_equals_dense(cfg1):
+    w, (q, k, v), (qf, kf, vf) = cfg1
+    cu = w.cu_seqlens
+    p = stem.Problem(cu, w.num_q_heads, w.num_kv_heads)
+    qd, kd, vd = to_dev(q, k, v)
+    fi, fc = O.full_lists(cu, w.num_q_heads, 128, q_block=64)
+    out = stem.stem_bsa_prefill_q64(p, qd, kd, vd, torch.from_numpy(fi).to(dev()),
+                                    torch.from_numpy(fc).to(dev()), SCALE)
+    do, _ = O.dense_causal_attention(qf, kf, vf, cu, w.num_q_heads, w.num_kv_heads, SCALE)
+    check_out(f64(out), do, BF16_MAX_ABS, BF16_MEAN_REL, "q64 all blocks vs dense")
