@@ -207,7 +207,6 @@ __global__ __launch_bounds__(256) void vprep_fp8_paged_kernel(const uint8_t *__r
 // ============================================================ work decode
 struct AttnItem {
   int h, g, r, z, I;
-  int half;                      // 64-query rows: which half of block row I (0 for square rows)
 };
 
 // Items are ordered by KV group, then by row from the last (longest causal
@@ -225,27 +224,6 @@ __device__ __forceinline__ AttnItem decode_attn(const AttnLaunch &a, const SeqTa
   w.r = t.row[0] + (rows - 1 - rr);
   w.z = seq_of(t.row, t.n, w.r);
   w.I = w.r - t.row[w.z];
-  w.half = 0;
-  return w;
-}
-
-// 64-query rows: the same order over twice as many rows.  List row r64 =
-// 2 r + half covers queries [64 half, 64 half + 64) of block row r; I is the
-// block row's index in its sequence (the key block holding the diagonal).
-__device__ __forceinline__ AttnItem decode_attn_q64(const AttnLaunch &a, const SeqTable &t, int rows) {
-  const int G = a.Hq / a.Hkv;
-  const int rows64 = 2 * rows;
-  const int item = xcd_chunk_item(blockIdx.x, rows64 * a.Hq);
-  const int slot = item / G, hh = item - slot * G;
-  AttnItem w;
-  w.g = slot / rows64;
-  const int rr = slot - w.g * rows64;
-  w.h = w.g * G + hh;
-  w.r = 2 * t.row[0] + (rows64 - 1 - rr);
-  const int r128 = w.r >> 1;
-  w.z = seq_of(t.row, t.n, r128);
-  w.I = r128 - t.row[w.z];
-  w.half = w.r & 1;
   return w;
 }
 
@@ -330,55 +308,115 @@ __device__ __forceinline__ float softmax_step(f32x16 (&s)[4], bool diag, int qlo
 // when a block's max exceeds it by more than 2^8 (weights stay <= 256, exact
 // range for fp16), which skips almost every rescale.
 //
-// kQ = 64 (64-query rows against 128-key blocks).  The same 8 waves, groups,
-// tiles and loads; a wave takes 32 queries (qw = w & 1) and one 32-key
-// sub-tile tw = (w >> 1) & 1 of its group's half, i.e. exactly the work of a
-// square-row wave restricted to one of its two key tiles: 8 S^T and 8 P.V
-// MFMAs per phase instead of 16 + 16.  The four key quarters of a query keep
-// separate online-softmax states, merged at the end.
+// kPair: 64 x 128 blocks (64-query rows, 128-key blocks).  A workgroup still
+// runs the 128-query tile of block row r, but each 64-query half has its own
+// list (list rows 2r and 2r + 1): the tile walks the ascending union of the
+// two lists, and a block that is not in a half's list gets zero weight for
+// that half's queries.  Waves qw = 0, 1 hold half 0 and qw = 2, 3 half 1, so
+// the test is wave-uniform and such a wave skips its softmax.  The union is
+// built once per workgroup in LDS (a bitmap per half, then one wave compacts
+// their OR in ascending order), so the block loop is the square-row loop.  On gfx950
+// this costs the same per listed block as square rows (measured equal on the
+// 128K layer), whereas a 64-query tile halves the MFMA work per K/V tile but
+// keeps the tile loads and barriers (measured 2.35x slower).
 constexpr float kLazyLog2 = 8.f;
 constexpr int kHalfK = 64 * kRow16;              // K half: 64 keys x 17 chunks (elements)
 constexpr int kRowVh = 72;                       // V^T half row: 64 keys + pad chunk (elements)
 constexpr int kHalfV = kHeadDim * kRowVh;        // V^T half: 128 dims x 9 chunks (elements)
 constexpr uint32_t kBufWord3 = 0x00020000u;      // raw buffer descriptor word 3 (gfx9 dword access)
 
-template <bool kSparse, int kQ>
+template <bool kSparse, bool kPair>
 __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTable t, int rows) {
-  static_assert(kQ == 128 || kQ == 64, "query rows of 128 or 64 tokens");
-  constexpr bool kQ64 = kQ == 64;
-  constexpr int NT = kQ64 ? 1 : 2;          // 32-key S^T tiles per wave
-  constexpr int NP = 8 * NT;                // P.V MFMAs per phase
-  constexpr int NM = 16 * NT;               // MFMAs per phase (P.V + S^T)
+  static_assert(kSparse || !kPair, "paired lists are block-sparse");
   __shared__ __attribute__((aligned(1024))) uint16_t K0[2 * kHalfK];   // bf16 K halves, [key][d]
   __shared__ __attribute__((aligned(1024))) uint16_t V0[2 * kHalfV];   // fp16 V^T halves, [d][key]
   __shared__ __attribute__((aligned(1024))) uint16_t K1[2 * kHalfK];
   __shared__ __attribute__((aligned(1024))) uint16_t V1[2 * kHalfV];
+  // kPair: union list (block | ownership << 16) and the two ownership bitmaps
+  __shared__ int32_t Ulist[kPair ? kMaxListBlocks : 1];
+  __shared__ uint32_t Ubits[kPair ? 2 * (kMaxListBlocks / 32) + 1 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int lg = lane >> 5, l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wg = wv & 3, kh = wv >> 2;      // wg: the wave's share of its group's loads
-  const int qw = kQ64 ? (wv & 1) : wg;      // 32-query slice
-  const int tw = kQ64 ? ((wv >> 1) & 1) : 0;
-  const AttnItem w = kQ64 ? decode_attn_q64(a, t, rows) : decode_attn(a, t, rows);
+  const int qw = wv & 3, kh = wv >> 2;
+  const AttnItem w = decode_attn(a, t, rows);
   const int zrow = t.row[w.z];
   const size_t ztok = (size_t)t.tok[w.z];
   const size_t qtok0 = ztok + (size_t)w.I * kBlock;
-  const int qloc = 64 * w.half + qw * 32 + l32;   // query offset in the diagonal block
+  const int qloc = qw * 32 + l32;
   const size_t qtok = qtok0 + qloc;
-  const size_t list_rows = kQ64 ? 2 * (size_t)a.R : (size_t)a.R;
-  cint32 *list = kSparse ? as_const(a.idx) + ((size_t)w.h * list_rows + w.r) * a.k_cap : nullptr;
+  // kPair: list rows 2r (queries 0-63) and 2r + 1 (queries 64-127)
+  const size_t lrow = kPair ? ((size_t)w.h * a.R + w.r) * 2 : (size_t)w.h * a.R + w.r;
+  cint32 *list = kSparse ? as_const(a.idx) + lrow * a.k_cap : nullptr;
   // Lists are trusted to be ascending in [0, I]; counts and ids are still
   // clamped so a malformed list can never address outside the sequence.
-  int n_blk = kSparse ? as_const(a.cnt)[(size_t)w.h * list_rows + w.r] : w.I + 1;
+  int n_blk = kSparse ? as_const(a.cnt)[lrow] : w.I + 1;
   if (kSparse && n_blk > a.k_cap) n_blk = a.k_cap;
+  int n_b = 0;
+  if constexpr (kPair) {
+    n_b = as_const(a.cnt)[lrow + 1];
+    if (n_b > a.k_cap) n_b = a.k_cap;
+    if (n_blk < 0) n_blk = 0;
+    if (n_b < 0) n_b = 0;
+  }
   __bf16 *orow = (__bf16 *)a.out + (qtok * a.Hq + w.h) * kHeadDim;
   float *lse = a.lse ? a.lse + (size_t)w.h * a.T + qtok : nullptr;
-  if (n_blk <= 0) {
-    if (kh == 0 && (!kQ64 || tw == 0)) write_empty(orow, lse, lg);   // the waves that hold results
+  if (n_blk + n_b <= 0) {
+    if (kh == 0) write_empty(orow, lse, lg);
     return;
   }
-  auto blk = [&](int b) { return kSparse ? (int)(list[b] < 0 ? 0 : (list[b] > w.I ? w.I : list[b])) : b; };
+  auto clampJ = [&](int J) { return J < 0 ? 0 : (J > w.I ? w.I : J); };
+  if constexpr (kPair) {
+    // Union of the two lists: set the ownership bits of every listed block
+    // (ids clamped into [0, I]), then wave 0 writes the set blocks in
+    // ascending order with their ownership (bit 0: list 2r, bit 1: 2r + 1).
+    const int nwords = (w.I + 1 + 31) >> 5;            // I < kMaxListBlocks (checked on the host)
+    for (int i = tid; i < 2 * nwords; i += 512) Ubits[i] = 0u;
+    __syncthreads();
+    cint32 *list_b = list + a.k_cap;
+    for (int i = tid; i < n_blk; i += 512) {
+      const int J = clampJ(list[i]);
+      atomicOr(&Ubits[J >> 5], 1u << (J & 31));
+    }
+    for (int i = tid; i < n_b; i += 512) {
+      const int J = clampJ(list_b[i]);
+      atomicOr(&Ubits[nwords + (J >> 5)], 1u << (J & 31));
+    }
+    __syncthreads();
+    if (tid < 64) {
+      int base = 0;
+      for (int c = 0; c < nwords; c += 64) {
+        const int wi = c + lane;
+        const uint32_t b0 = wi < nwords ? Ubits[wi] : 0u, b1 = wi < nwords ? Ubits[nwords + wi] : 0u;
+        uint32_t bits = b0 | b1;
+        const int n = __popc(bits);
+        int incl = n;                                  // inclusive scan over the wave
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+          const int y = __shfl_up(incl, d, 64);
+          if (lane >= d) incl += y;
+        }
+        int pos = base + incl - n;
+        while (bits) {
+          const int bb = __ffs(bits) - 1;
+          bits &= bits - 1;
+          Ulist[pos++] = (32 * wi + bb) | (int)(((b0 >> bb) & 1u) | (((b1 >> bb) & 1u) << 1)) << 16;
+        }
+        base += __shfl(incl, 63, 64);
+      }
+      if (lane == 0) Ubits[2 * (kMaxListBlocks / 32)] = (uint32_t)base;
+    }
+    __syncthreads();
+    n_blk = __builtin_amdgcn_readfirstlane((int)Ubits[2 * (kMaxListBlocks / 32)]);
+  }
+  // Block id b of the walk (kPair: its union entry, ownership in bits 16-17).
+  auto blk_entry = [&](int b) __attribute__((always_inline)) {
+    if constexpr (kPair) return __builtin_amdgcn_readfirstlane(Ulist[b]);
+    else return kSparse ? clampJ(list[b]) : b;
+  };
+  auto blk = [&](int b) __attribute__((always_inline)) { return blk_entry(b) & 0xffff; };
+  const int my_bit = qw < 2 ? 1 : 2;
 
   // Q as the B operand: query qloc, head dims 16 ks + 8 lg .. +7
   bf16x8 qf[8];
@@ -396,14 +434,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
   //   V half: 18 loads; slot s -> dim row s / 9, chunk s % 9 of this half's
   //           8 image chunks (chunk 8 is the pad and re-reads chunk 0).
   const uint32_t kstride_b = (uint32_t)a.Hkv * kHeadDim * 2;
-  const int nkk = wg == 0 ? 5 : 4, nkv = wg < 2 ? 5 : 4;
+  const int nkk = qw == 0 ? 5 : 4, nkv = qw < 2 ? 5 : 4;
   uint32_t koff[5], voff[5];
 #pragma unroll
   for (int m = 0; m < 5; ++m) {
-    const int sk = 64 * (wg + 4 * m) + lane;
+    const int sk = 64 * (qw + 4 * m) + lane;
     const int rk = sk / 17, ck = sk - 17 * rk;
     koff[m] = (uint32_t)rk * kstride_b + 16 * (ck < 16 ? ck : 0);
-    const int sv = 64 * (wg + 4 * m) + lane;
+    const int sv = 64 * (qw + 4 * m) + lane;
     const int rv = sv / 9, cv = sv - 9 * rv;
     voff[m] = (uint32_t)(rv * kRow16 * 2 + 16 * (8 * kh + (cv < 8 ? cv : 0)));
   }
@@ -417,7 +455,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
     uint16_t *d = Kd + kh * kHalfK;
 #pragma unroll
     for (int m = 0; m < 5; ++m)
-      if (m < nkk) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(d + (wg + 4 * m) * 512), 16, koff[m], 0, 0, 0);
+      if (m < nkk) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(d + (qw + 4 * m) * 512), 16, koff[m], 0, 0, 0);
   };
   // The loads of one block step: d = 0..4 are K loads m = d of the next
   // block (a descriptor of size 0 when there is none: no memory is read and
@@ -438,8 +476,8 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
   f32x16 o[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) o[u] = f32x16{};
-  f32x16 s[NT];           // S^T of the current block (this wave's 64 or 32 keys)
-  u32x4 pk[2 * NT];       // P of the previous block, fp16, one 16-key step each
+  f32x16 s[2];            // S^T of the current block (this wave's 64 keys)
+  u32x4 pk[4];            // P of the previous block, fp16, one 16-key step each
 
   // MFMA phase: P.V of the previous block (if kPV) from the V^T half in Vp,
   // then S^T of this block from the K half in Kc, as one stream of MFMAs
@@ -456,40 +494,31 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
     uint16_t *dk = Kn + kh * kHalfK, *dv = Vc + kh * kHalfV;
     auto dma = [&](int d) __attribute__((always_inline)) {
       if (d < 5) {
-        if (d < nkk) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_ptr(dk + (wg + 4 * d) * 512), 16, koff[d], 0, 0, 0);
+        if (d < nkk) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_ptr(dk + (qw + 4 * d) * 512), 16, koff[d], 0, 0, 0);
       } else {
         const int m = d - 5;
-        if (m < nkv) __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_ptr(dv + (wg + 4 * m) * 512), 16, voff[m], 0, 0, 0);
+        if (m < nkv) __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_ptr(dv + (qw + 4 * m) * 512), 16, voff[m], 0, 0, 0);
       }
     };
-    constexpr int i0 = PV ? 0 : NP;
-    // kQ = 64: the wave's key tile tw is 32 K rows further and two 16-key
-    // steps further along the V^T rows
-    const uint16_t *vad = Vp + kh * kHalfV + l32 * kRowVh + 8 * lg + 32 * tw;
-    const uint16_t *kad = Kc + kh * kHalfK + l32 * kRow16 + 8 * lg + 32 * kRow16 * tw;
+    constexpr int i0 = PV ? 0 : 16;
+    const uint16_t *vad = Vp + kh * kHalfV + l32 * kRowVh + 8 * lg;
+    const uint16_t *kad = Kc + kh * kHalfK + l32 * kRow16 + 8 * lg;
     auto rd = [&](int i) __attribute__((always_inline)) {
-      return i < NP ? ld16(vad + 32 * kRowVh * (i & 3) + 16 * (i >> 2))
-                    : ld16(kad + 32 * kRow16 * ((i - NP) % NT) + 16 * ((i - NP) / NT));
+      return i < 16 ? ld16(vad + 32 * kRowVh * (i & 3) + 16 * (i >> 2))
+                    : ld16(kad + 32 * kRow16 * ((i - 16) & 1) + 16 * ((i - 16) >> 1));
     };
-    u32x4 r[NM];
+    u32x4 r[32];
 #pragma unroll
     for (int i = i0; i < i0 + kAhead; ++i) r[i] = rd(i);
 #pragma unroll
-    for (int i = i0; i < NM; ++i) {
-      if (i + kAhead < NM) r[i + kAhead] = rd(i + kAhead);
-      if constexpr (!kQ64) {
-        if (PV ? (i % 3 == 1 && i < 30) : (i - 16 < 10)) dma(PV ? i / 3 : i - 16);
-      } else if (PV) {
-        if (i < 10) dma(i);                  // 10 loads over 16 MFMAs
-      } else if (i - NP < 5) {
-        dma(2 * (i - NP));                   // 10 loads over 8 MFMAs
-        dma(2 * (i - NP) + 1);
-      }
+    for (int i = i0; i < 32; ++i) {
+      if (i + kAhead < 32) r[i + kAhead] = rd(i + kAhead);
+      if (PV ? (i % 3 == 1 && i < 30) : (i - 16 < 10)) dma(PV ? i / 3 : i - 16);
       __builtin_amdgcn_sched_barrier(0);
-      if (i < NP) {
+      if (i < 16) {
         o[i & 3] = mfma_f16_32x32x16(as_f16x8(r[i]), as_f16x8(pk[i >> 2]), o[i & 3]);
       } else {
-        const int tt = (i - NP) % NT, ks = (i - NP) / NT;
+        const int tt = (i - 16) & 1, ks = (i - 16) >> 1;
         s[tt] = mfma_bf16_32x32x16(as_bf16x8(r[i]), qf[ks], ks == 0 ? f32x16{} : s[tt]);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -497,13 +526,13 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
   };
   // P.V of the last block (no S^T after it).
   auto pv_last = [&](const uint16_t *Vp) __attribute__((always_inline)) {
-    const uint16_t *vad = Vp + kh * kHalfV + l32 * kRowVh + 8 * lg + 32 * tw;
-    u32x4 r[NP];
+    const uint16_t *vad = Vp + kh * kHalfV + l32 * kRowVh + 8 * lg;
+    u32x4 r[16];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) r[i] = ld16(vad + 32 * kRowVh * (i & 3) + 16 * (i >> 2));
 #pragma unroll
-    for (int i = 0; i < NP; ++i) {
-      if (i + kAhead < NP) r[i + kAhead] = ld16(vad + 32 * kRowVh * ((i + kAhead) & 3) + 16 * ((i + kAhead) >> 2));
+    for (int i = 0; i < 16; ++i) {
+      if (i + kAhead < 16) r[i + kAhead] = ld16(vad + 32 * kRowVh * ((i + kAhead) & 3) + 16 * ((i + kAhead) >> 2));
       __builtin_amdgcn_sched_barrier(0);
       o[i & 3] = mfma_f16_32x32x16(as_f16x8(r[i]), as_f16x8(pk[i >> 2]), o[i & 3]);
       __builtin_amdgcn_sched_barrier(0);
@@ -514,18 +543,23 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
   // in this half).  A query can see no key at all in this half (diagonal
   // block, keys 64-127, queries < 64): its max stays -inf, alpha stays 1 and
   // the exponent offset is 0, so every weight is 0.
-  auto softmax = [&](bool diag) __attribute__((always_inline)) {
-    if (diag) {
-      const int lim = qloc - 64 * kh - 32 * tw - 4 * lg;   // key > qloc  <=>  local key offset > lim
+  auto softmax = [&](bool diag, bool off) __attribute__((always_inline)) {
+    if (off) {                     // kPair: not in this half's list, zero weight
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt)
+      for (int cc = 0; cc < 4; ++cc) pk[cc] = u32x4{0u, 0u, 0u, 0u};
+      return;
+    }
+    if (diag) {
+      const int lim = qloc - 64 * kh - 4 * lg;        // key > qloc  <=>  local key offset > lim
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
           s[tt][i] = (32 * tt + 8 * (i >> 2) + (i & 3) > lim) ? -INFINITY : s[tt][i];
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[tt][i]);
     mx = wave_max_xor32(mx) * c;
@@ -542,7 +576,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
 #pragma unroll
-    for (int tt = 0; tt < NT; ++tt)
+    for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         s[tt][i] = __builtin_amdgcn_exp2f(fmaf(s[tt][i], c, -m_use));
@@ -550,7 +584,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
       }
     l_run += psum;
 #pragma unroll
-    for (int cc = 0; cc < 2 * NT; ++cc) {
+    for (int cc = 0; cc < 4; ++cc) {
       const int tt = cc >> 1, j0 = 8 * (cc & 1);
       pk[cc] = u32x4{pack_f16x2(s[tt][j0 + 0], s[tt][j0 + 1]), pack_f16x2(s[tt][j0 + 2], s[tt][j0 + 3]),
                      pack_f16x2(s[tt][j0 + 4], s[tt][j0 + 5]), pack_f16x2(s[tt][j0 + 6], s[tt][j0 + 7])};
@@ -559,19 +593,23 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
 
   // Block b: [wait, barrier, loads for b+1, M_b, barrier, X_b].  Block b
   // uses K[b % 2] and V[b % 2]; P.V of block b-1 reads V[(b-1) % 2].
+  int own = 0;                       // kPair: ownership of the current block in bits 16-17
   auto step = [&](auto kPV, int b, int &J, const uint16_t *Kc, const uint16_t *Vp, uint16_t *Kn, uint16_t *Vc)
                   __attribute__((always_inline)) {
-    const int Jn = b + 1 < n_blk ? blk(b + 1) : 0;
+    const int en = b + 1 < n_blk ? blk_entry(b + 1) : 0;
+    const int Jn = kPair ? (en & 0xffff) : en;
     wait_vmcnt<0>();                 // this wave's K of b and V of b-1 have landed
     block_sync();                    // ... the whole group's too; Kn and Vc are free
     mfma_phase(kPV, Vp, Kc, k_rsrc(Jn, b + 1 < n_blk), v_rsrc(J), Kn, Vc);
     block_sync();
-    softmax(J == w.I);
+    softmax(J == w.I, kPair && ((own >> 16) & my_bit) == 0);
     J = Jn;
+    own = en;
   };
   using NoPV = std::integral_constant<bool, false>;
   using WithPV = std::integral_constant<bool, true>;
 
+  if constexpr (kPair) own = blk_entry(0);
   int J = blk(0);
   issue_k(J, K0);
   if (kh == 1) block_sync();         // group 1 runs one phase behind
@@ -589,48 +627,6 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
   pv_last((n_blk & 1) ? V0 : V1);
   if (kh == 0) block_sync();         // realign the groups
 
-  if constexpr (kQ64) {
-    // merge the four key quarters kq = 2 kh + tw of each query slice: waves
-    // with kq = 1..3 hand (O, m, l) to the kq = 0 wave through LDS (six
-    // 66 x 64-float buffers, two per K/V array)
-    block_sync();
-    auto xbuf = [&](int j) __attribute__((always_inline)) {       // j = 3 qw + kq - 1
-      float *base = (float *)(j < 2 ? K0 : (j < 4 ? V0 : K1));
-      return base + (j & 1) * (66 * 64);
-    };
-    const int kq = 2 * kh + tw;
-    if (kq != 0) {
-      float *xch = xbuf(3 * qw + kq - 1);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) xch[(16 * u + i) * 64 + lane] = o[u][i];
-      xch[64 * 64 + lane] = m_run;
-      xch[65 * 64 + lane] = l_run;
-    }
-    block_sync();
-    if (kq == 0) {
-      const float *x1 = xbuf(3 * qw), *x2 = xbuf(3 * qw + 1), *x3 = xbuf(3 * qw + 2);
-      const float m1 = x1[64 * 64 + lane], m2 = x2[64 * 64 + lane], m3 = x3[64 * 64 + lane];
-      // finite: the query's own key, or every key of an earlier listed block, is visible
-      const float m = fmaxf(fmaxf(m_run, m1), fmaxf(m2, m3));
-      auto wgt = [&](float mi) { return mi == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mi - m); };
-      const float a0 = wgt(m_run), a1 = wgt(m1), a2 = wgt(m2), a3 = wgt(m3);
-      float l = l_run * a0 + x1[65 * 64 + lane] * a1 + x2[65 * 64 + lane] * a2 + x3[65 * 64 + lane] * a3;
-      l += __shfl_xor(l, 32, 64);
-      const float inv = 1.f / l;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int e = (16 * u + i) * 64 + lane;
-          o[u][i] = (o[u][i] * a0 + x1[e] * a1 + x2[e] * a2 + x3[e] * a3) * inv;
-        }
-      write_out(orow, o, 1.f, lg);
-      if (lse && lg == 0) *lse = (m + __log2f(l)) * 0.69314718055994531f;
-    }
-    return;
-  }
   // merge the two key halves: waves 4-7 hand (O, m, l) to waves 0-3 through LDS
   block_sync();
   float *xch = (float *)(qw < 2 ? K0 : K1) + (qw & 1) * (66 * 64);
@@ -651,13 +647,14 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
     const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
     float l = l_run * a0 + l1 * a1;
     l += __shfl_xor(l, 32, 64);
-    const float inv = 1.f / l;
+    // kPair: a half whose list is empty sees no key (l = 0): output 0, lse -inf
+    const float inv = kPair ? (l > 0.f ? 1.f / l : 0.f) : 1.f / l;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[u][i] = (o[u][i] * a0 + xch[(16 * u + i) * 64 + lane] * a1) * inv;
     write_out(orow, o, 1.f, lg);
-    if (lse && lg == 0) *lse = (m + __log2f(l)) * 0.69314718055994531f;
+    if (lse && lg == 0) *lse = kPair && !(l > 0.f) ? -INFINITY : (m + __log2f(l)) * 0.69314718055994531f;
   }
 }
 
@@ -905,15 +902,15 @@ hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows, bool sp
     if (sparse) hipLaunchKernelGGL(attn_fp8_kernel<true>, grid, dim3(256), 0, s, a, t, rows);
     else hipLaunchKernelGGL(attn_fp8_kernel<false>, grid, dim3(256), 0, s, a, t, rows);
   } else {
-    if (sparse) hipLaunchKernelGGL((attn_bf16_kernel<true, 128>), grid, dim3(512), 0, s, a, t, rows);
-    else hipLaunchKernelGGL((attn_bf16_kernel<false, 128>), grid, dim3(512), 0, s, a, t, rows);
+    if (sparse) hipLaunchKernelGGL((attn_bf16_kernel<true, false>), grid, dim3(512), 0, s, a, t, rows);
+    else hipLaunchKernelGGL((attn_bf16_kernel<false, false>), grid, dim3(512), 0, s, a, t, rows);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_attn_q64(const AttnLaunch &a, const SeqTable &t, int rows, hipStream_t s) {
-  const dim3 grid(2 * rows * a.Hq);
-  hipLaunchKernelGGL((attn_bf16_kernel<true, 64>), grid, dim3(512), 0, s, a, t, rows);
+  const dim3 grid(rows * a.Hq);
+  hipLaunchKernelGGL((attn_bf16_kernel<true, true>), grid, dim3(512), 0, s, a, t, rows);
   return hipGetLastError();
 }
 

@@ -232,6 +232,7 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
     return STEM_ERR_UNSUPPORTED;
   }
   if (sparse && (!block_idx || !block_cnt || k_cap < 1)) return STEM_ERR_INVALID_ARG;
+  if (q64 && s.max_nb > kMaxListBlocks) return STEM_ERR_UNSUPPORTED;
   const size_t need = attn_workspace_bytes(s.Hkv, s.R, fp8);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return STEM_ERR_WORKSPACE;
 

@@ -226,9 +226,11 @@ int stem_bsa_prefill_paged(const stem_problem_t *p, const void *q, const void *k
  * q, k, v: bf16 as in stem_bsa_prefill; out, lse, softmax_scale, workspace
  *   (stem_attn_workspace_bytes(p, BF16)) likewise.  Precision as the bf16
  *   path of stem_bsa_prefill.
- * Giving both halves of a row the row's list reproduces stem_bsa_prefill up
- * to fp32 summation order.
- * Errors: as stem_bsa_prefill with dtype BF16.
+ * Giving both halves of a row the row's list reproduces stem_bsa_prefill
+ * (bit for bit: the kernel runs the row's 128 queries over the union of the
+ * two lists and gives a block zero weight in a half that does not list it).
+ * Errors: as stem_bsa_prefill with dtype BF16; UNSUPPORTED for a sequence
+ * longer than 4096 key blocks (512K tokens).
  * ------------------------------------------------------------------------- */
 int stem_bsa_prefill_q64(const stem_problem_t *p, const void *q, const void *k, const void *v,
                          const int32_t *block_idx, const int32_t *block_cnt, int32_t k_cap,

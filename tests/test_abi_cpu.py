@@ -173,6 +173,7 @@ def test_q64_attention_argument_errors():
     assert call(p.ref, f, f, f, f, f, 8, -1.0, f, None, f, W, None) == 1          # scale
     assert call(p.ref, f, f, f, f, f, 8, 0.1, f, None, f, 100, None) == 4         # workspace size
     assert call(stem.Problem([0, 1000], 4, 2).ref, f, f, f, f, f, 8, 0.1, f, None, f, W, None) == 2
+    assert call(stem.Problem([0, 128 * 4097], 4, 2).ref, f, f, f, f, f, 8, 0.1, f, None, f, W, None) == 2
 
 
 def test_package_defaults_match_the_doc_table():
