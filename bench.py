@@ -293,7 +293,7 @@ def run_main(args):
         "speedup_vs_dense": t_dense / t_stem,
         "bsa_speedup_vs_dense": t_dense / timer.mean("bsa"),
         "skip_overhead": timer.mean("bsa") / (rho * t_dense) - 1.0,
-        "tile_64x128": {"kernel": "attn_bf16_kernel<sparse, 64-query rows>", "bsa_ms": dtimer.mean("q64"),
+        "tile_64x128": {"kernel": "attn_bf16_kernel<sparse, paired 64-query lists>", "bsa_ms": dtimer.mean("q64"),
                         "vs_128x128": dtimer.mean("q64") / timer.mean("bsa"),
                         "tflops": bsa_flop / (dtimer.mean("q64") * 1e-3) / 1e12},
         "score_mfma_tflops": score_flop / (timer.mean("score") * 1e-3) / 1e12,
