@@ -247,13 +247,23 @@ __device__ __forceinline__ void write_empty(__bf16 *orow, float *lse, int lg) {
   if (lse && lg == 0) *lse = -INFINITY;
 }
 
-// Online-softmax step on the raw S^T accumulators (lane = one query, 64 of
-// its 128 keys; the other 64 sit in lane ^ 32).  c = this block's logit
-// scale times log2 e (> 0), so the block max is c * max(raw) and every weight
-// is one fma + exp2.  The running max m_run is kept in scaled (log2) units.
-// Leaves p = 2^(c s - m) in s and returns the rescale factor of O.
-__device__ __forceinline__ float softmax_step(f32x16 (&s)[4], bool diag, int qloc, int lg, float c,
-                                              float &m_run, float &l_run) {
+// Online-softmax step of the fp8 kernel on the raw S^T accumulators (lane =
+// one query, 64 of its 128 keys; the other 64 sit in lane ^ 32).  c = the
+// block's logit scale times log2 e (> 0); lv = log2 of the block's V scale.
+// The V scale is folded into the weights: the MFMA operand for key k is
+//   P'_k = 2^(c s_k + lv - R + kFp8Off),
+// so O accumulates P' times the raw V codes, and L accumulates P'_k / vs,
+// i.e. 2^(c s_k - R + kFp8Off).  Then O / L is the output and
+// R - kFp8Off + log2 L the log2-sum-exp.  The reference R is raised only when
+// a block's largest log-weight c s + lv exceeds it by more than kFp8Lazy
+// (O and L are then rescaled), so P' <= 2^(kFp8Off + kFp8Lazy) = 430 < 448
+// (the e4m3 maximum) while the largest weight seen so far keeps
+// P' >= 2^(kFp8Off - kFp8Lazy) = 152: small weights stay in e4m3's normal
+// range as far down as with P' = 256 p.  O is rarely touched.  Leaves P' in s.
+constexpr float kFp8Lazy = 0.75f;
+constexpr float kFp8Off = 8.f;
+__device__ __forceinline__ void softmax_fp8(f32x16 (&s)[4], bool diag, int qloc, int lg, float c, float lv,
+                                            float inv_vs, float &R, float &L, f32x16 (&o)[4]) {
   if (diag) {
     const int lim = qloc - 4 * lg;          // key > qloc  <=>  (key - 4 lg) > lim
 #pragma unroll
@@ -267,21 +277,30 @@ __device__ __forceinline__ float softmax_step(f32x16 (&s)[4], bool diag, int qlo
   for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[tt][i]);
-  mx = wave_max_xor32(mx);
-  const float m_new = fmaxf(m_run, mx * c);
-  const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-  m_run = m_new;
+  // every query sees at least one key of the block (all of an earlier block,
+  // itself in the diagonal one), so mz is finite
+  const float mz = fmaf(wave_max_xor32(mx), c, lv);
+  if (__any(mz > R + kFp8Lazy)) {
+    const float Rn = fmaxf(R, mz);
+    const float f = __builtin_amdgcn_exp2f(R - Rn);   // 0 on the first block (R = -inf), else <= 1
+    R = Rn;
+    L *= f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[u][i] *= f;
+  }
+  const float off = lv - R + kFp8Off;
   float psum = 0.f;
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(s[tt][i], c, -m_new));
+      const float p = __builtin_amdgcn_exp2f(fmaf(s[tt][i], c, off));
       s[tt][i] = p;
       psum += p;
     }
-  l_run = l_run * alpha + psum;
-  return alpha;
+  L = fmaf(psum, inv_vs, L);
 }
 
 // ===================================================================== bf16
@@ -660,12 +679,11 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
 
 // ====================================================================== fp8
 // Same pipeline on e4m3 operands with the 32x32x64 fp8 MFMA: Q.K^T in two
-// K=64 steps per key tile, P quantised to e4m3 as p * 2^8 (p <= 1, so the
-// largest code is 256 < 448 and fewer small weights flush to zero), P.V in
-// two K=64 steps per head-dim tile.  Per-block scales: the q and k scales
-// fold into the exponent scale c of the block; the v scale of block J is
-// applied by keeping O in units of the current block's v scale (one multiply
-// merged with the online-softmax rescale).  The diagonal block, where the
+// K=64 steps per key tile, P quantised to e4m3 (at most 256 < 448, see
+// softmax_fp8), P.V in two K=64 steps per head-dim tile.  Per-block scales:
+// the q and k scales fold into the exponent scale c of the block, the v
+// scale into the exponent offset of the weights (softmax_fp8), so no
+// per-element multiply is spent on either.  The diagonal block, where the
 // first queries of a sequence see only a few keys and 3-bit weights would not
 // average out, runs its P.V in fp16 from the exact fp16 V^T image.
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
@@ -765,7 +783,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
 
-  float m_run = -INFINITY, l_run = 0.f, vs_run = 1.f;
+  float R = -INFINITY, L = 0.f;      // softmax_fp8's reference and weight sum
   f32x16 o[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) o[u] = f32x16{};
@@ -789,13 +807,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
       for (int ks = 0; ks < 2; ++ks)
         s[tt] = mfma_fp8_32x32x64(ld32(k8ad + 32 * kRow8 * tt + 64 * ks), qf[ks], s[tt]);
     }
-    const float alpha = softmax_step(s, diag, qloc, lg, c, m_run, l_run);
-    const float f = alpha * (vs_run / vs);
-    vs_run = vs;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[u][i] *= f;
+    softmax_fp8(s, diag, qloc, lg, c, __builtin_amdgcn_logf(vs), __builtin_amdgcn_rcpf(vs), R, L, o);
     wait_vmcnt<0>();
     block_sync();
     if (kNext != kNone) issue_k(Jn);
@@ -808,8 +820,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const f32x16 &st = s[2 * cc + aa];
-            pk[4 * aa + j] = (int)pack_fp8x4(st[4 * j + 0] * 256.f, st[4 * j + 1] * 256.f,
-                                             st[4 * j + 2] * 256.f, st[4 * j + 3] * 256.f);
+            pk[4 * aa + j] = (int)pack_fp8x4(st[4 * j + 0], st[4 * j + 1], st[4 * j + 2], st[4 * j + 3]);
           }
 #pragma unroll
         for (int u = 0; u < 4; ++u)
@@ -819,10 +830,8 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
         const int tt = cc >> 1, j0 = 8 * (cc & 1);
-        const u32x4 v4 = {pack_f16x2(s[tt][j0 + 0] * 256.f, s[tt][j0 + 1] * 256.f),
-                          pack_f16x2(s[tt][j0 + 2] * 256.f, s[tt][j0 + 3] * 256.f),
-                          pack_f16x2(s[tt][j0 + 4] * 256.f, s[tt][j0 + 5] * 256.f),
-                          pack_f16x2(s[tt][j0 + 6] * 256.f, s[tt][j0 + 7] * 256.f)};
+        const u32x4 v4 = {pack_f16x2(s[tt][j0 + 0], s[tt][j0 + 1]), pack_f16x2(s[tt][j0 + 2], s[tt][j0 + 3]),
+                          pack_f16x2(s[tt][j0 + 4], s[tt][j0 + 5]), pack_f16x2(s[tt][j0 + 6], s[tt][j0 + 7])};
         const f16x8 pk = as_f16x8(v4);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
@@ -862,9 +871,9 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
     else step(J, 0, kNone, false, false);
   }
 
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-  write_out(orow, o, vs_run / (256.f * l_tot), lg);
-  if (lse && lg == 0) *lse = (m_run + __log2f(l_tot)) * 0.69314718055994531f;
+  const float l_tot = L + __shfl_xor(L, 32, 64);
+  write_out(orow, o, 1.f / l_tot, lg);
+  if (lse && lg == 0) *lse = (R - kFp8Off + __log2f(l_tot)) * 0.69314718055994531f;
 }
 
 // ================================================================ launchers
