@@ -21,6 +21,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -59,10 +60,16 @@ def bsa_pairs(idx, cnt, p):
 
 
 def source_sha(*names):
+    """Hash of the kernel sources with comments and whitespace removed: a
+    measured traffic figure stays valid across comment edits and goes stale
+    with any change to the code itself."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "block_sparse_attention_stem_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "block_sparse_attention_stem_amd", "csrc", n)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update("".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

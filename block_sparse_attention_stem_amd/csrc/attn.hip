@@ -7,32 +7,35 @@
 // skipped block is equivalent to -inf scores, so online softmax over just the
 // listed blocks is exact.
 //
-// Design (per workgroup of 4 waves = one (query head h, query block I), 32
-// queries per wave):
+// Design shared by the kernels below (one workgroup = one (query head h,
+// query block row I); each wave holds 32 queries):
 //  * Everything is computed transposed so a query lives on a lane:
 //    S^T = K Q^T (A = K rows from LDS, B = the wave's Q in registers), then
 //    O^T += V^T P^T (A = V^T rows from LDS, B = P^T packed straight from the
 //    S^T accumulators).  With the 32x32 MFMA output layout lane l owns query
 //    l % 32 in every accumulator: the row max is one cross-half exchange and
 //    the O rescale is a per-lane scalar.
-//  * K and V tiles reach LDS through asynchronous direct loads
-//    (global_load_lds_dwordx4): no staging registers, no staging VALU.  Each
-//    1 KB instruction fills 64 consecutive 16-byte LDS slots, and each lane
-//    may fetch any global chunk, so tiles are laid out with one pad chunk per
-//    row (rows of 17 chunks for 256-byte rows, 9 for 128-byte rows; a pad
-//    slot re-reads a valid chunk).  Row r then starts 4 (r mod 16) banks
-//    further along the 64-bank LDS, so the 16 lanes served together (16
+//  * K and V tiles reach LDS through asynchronous direct loads (buffer or
+//    global loads with the lds modifier): no staging registers, no staging
+//    VALU.  Each 1 KB instruction fills 64 consecutive 16-byte LDS slots, and
+//    each lane may fetch any global chunk, so tiles are laid out with one pad
+//    chunk per row (rows of 17 chunks for 256-byte rows, 9 for 128-byte
+//    rows; a pad slot re-reads a valid chunk).  Row r then starts 4 (r mod 16)
+//    banks further along the 64-bank LDS, so the 16 lanes served together (16
 //    consecutive rows, same column) never collide, and every operand read of
 //    a lane is one base address plus immediate offsets.
 //  * V^T cannot be produced by a plain copy, so a pre-pass writes each V block
 //    once per call as the exact LDS image: transposed, keys permuted into the
-//    order the S^T accumulators hold them, swizzled, and (bf16 path) converted
+//    order the S^T accumulators hold them, padded, and (bf16 path) converted
 //    to fp16, which is exact for bf16 values in fp16's range.  P.V then uses
 //    fp16 weights (11 significant bits instead of bf16's 8).
-//  * The next listed block's K is requested right after the current block's
-//    K reads end and its V right after the V reads end, so every load has a
-//    whole compute phase to land; the list is read one entry ahead and the
-//    inner loop never tests whether a block is kept.
+//  * Loads for the next listed block are issued while the current one
+//    computes, the list is read one entry ahead, and the inner loop never
+//    tests whether a block is kept.
+//  * bf16: 8 waves in two groups that split each block's keys and run one
+//    phase apart (MFMA phase of one wave beside the softmax of the other on
+//    each SIMD), one workgroup per CU.  fp8: 4 waves over all 128 keys, two
+//    workgroups per CU.
 #include <type_traits>
 
 #include "stem_internal.h"

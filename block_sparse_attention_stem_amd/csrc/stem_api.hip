@@ -280,7 +280,7 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
     SeqTable t;
     fill_table(p, z0, n, &t);
     const int rows = t.row[n] - t.row[0];
-    if ((int64_t)rows * s.Hq * (q64 ? 2 : 1) >= ((int64_t)1 << 31)) return STEM_ERR_UNSUPPORTED;
+    if ((int64_t)rows * s.Hq >= ((int64_t)1 << 31)) return STEM_ERR_UNSUPPORTED;
     if (table && launch_vprep_paged(a, t, rows, hs) != hipSuccess) return STEM_ERR_HIP;
     const hipError_t e = q64 ? launch_attn_q64(a, t, rows, hs) : launch_attn(a, t, rows, sparse, fp8, hs);
     if (e != hipSuccess) return STEM_ERR_HIP;
