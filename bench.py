@@ -287,7 +287,7 @@ def run_main(args):
     score_flop = 2.0 * 16 * 16 * 1024 * causal_blocks
     bsa_tflops = bsa_flop / (timer.mean("bsa") * 1e-3) / 1e12
     topk_bytes = 4.0 * causal_blocks + 4.0 * (idx.numel() + cnt.numel())
-    traffic = load_traffic("attn_bf16_sparse_cfg3", source_sha("attn.hip", "gfx950_util.h"))
+    traffic = load_traffic("attn_bf16_sparse_n128k", source_sha("attn.hip", "gfx950_util.h"))
 
     res = {
         "metric": METRIC,
@@ -297,7 +297,7 @@ def run_main(args):
         "ms_per_step": t_stem,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "cfg3: one attention layer, batch 1, N=131072, 32 q heads / 8 kv heads, "
+        "config": {"workload": "one attention layer, batch 1, N=131072, 32 q heads / 8 kv heads, "
                                "head_dim 128, bf16 N(0,1) Q/K/V with +3 sigma sink keys and lognormal V "
                                "rows; block 128, stride 8, chunk 2048, beta 0.2, k_start 276, alpha 0.7, "
                                "mu 0.5, 1 sink + 2 window blocks",
@@ -411,7 +411,7 @@ def fp8_varlen(args, torch, stem, S, dev):
         L_["skip_overhead"] = L_["stages_ms"]["bsa"] / (L_["computed_pair_fraction"] * t_dense) - 1.0
     total = 5 * layers["alpha_1.0"]["ms"] + 31 * lo["ms"]
     log(f"[bench]   fp8 dense {t_dense:.2f} ms; 36 layers {total:.1f} ms vs dense {36 * t_dense:.1f} ms")
-    return {"workload": "cfg5: fp8 e4m3 varlen, seqlens 8192/16384/32768/73728 (T=131072), 32q/8kv, "
+    return {"workload": "fp8 e4m3 varlen, seqlens 8192/16384/32768/73728 (T=131072), 32q/8kv, "
                         "d128, per-(128-block, head) scales, k_start 18/35/70/156, mu 0.5, 1 sink + 2 window",
             "layers": layers, "dense_ms": t_dense,
             "dense_tflops": flop_dense / (t_dense * 1e-3) / 1e12,
@@ -573,7 +573,7 @@ def density_sweep(args, torch, stem, S, dev):
     a = my - b * mx
     ss_res = sum((y - (a + b * x)) ** 2 for x, y in zip(xs, ys))
     ss_tot = sum((y - my) ** 2 for y in ys)
-    return {"workload": "cfg4: N=65536, 32q/8kv, d128, alpha 0.7, mu 0.5, 1 sink + 2 window",
+    return {"workload": "N=65536, 32q/8kv, d128, alpha 0.7, mu 0.5, 1 sink + 2 window",
             "dense_ms": t_dense, "points": pts,
             "linear_fit_ms": {"intercept": a, "slope": b, "r2": 1 - ss_res / ss_tot}}
 
@@ -583,7 +583,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="cfg3_n128k")
+    ap.add_argument("--workload", default="n128k_32q8kv")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--length-sweep", action="store_true",

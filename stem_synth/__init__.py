@@ -72,14 +72,14 @@ def cu_from_lengths(lengths: Sequence[int]) -> List[int]:
 # block-pair fraction is closest to the target density.
 CONFIGS = {
     # 2 query heads share 1 KV head, N = 2048; 8 of 16 key blocks at the start.
-    "cfg1_n2k": Workload("cfg1_n2k", (2048,), 2, 1, seed=0, sink=False,
-                         k_start=(8,), mu=0.5, alpha=1.0, n_init=1, n_window=1),
+    "n2k_2q1kv": Workload("n2k_2q1kv", (2048,), 2, 1, seed=0, sink=False,
+                          k_start=(8,), mu=0.5, alpha=1.0, n_init=1, n_window=1),
     # Qwen3-8B-shaped layer at 32K, keep ~25 %.
-    "cfg2_n32k": Workload("cfg2_n32k", (32768,), 32, 8, seed=0, k_start=(70,),
-                          mu=0.5, alpha=0.7, n_init=1, n_window=2),
+    "n32k_32q8kv": Workload("n32k_32q8kv", (32768,), 32, 8, seed=0, k_start=(70,),
+                            mu=0.5, alpha=0.7, n_init=1, n_window=2),
     # The 128K headline shape, keep ~25 %.
-    "cfg3_n128k": Workload("cfg3_n128k", (131072,), 32, 8, seed=0, k_start=(276,),
-                           mu=0.5, alpha=0.7, n_init=1, n_window=2),
+    "n128k_32q8kv": Workload("n128k_32q8kv", (131072,), 32, 8, seed=0, k_start=(276,),
+                             mu=0.5, alpha=0.7, n_init=1, n_window=2),
 }
 
 # Density sweep at N = 65536: target keep ratio -> k_start (same derivation).
@@ -87,7 +87,7 @@ SWEEP_N64K = {1.00: 1461, 0.50: 322, 0.25: 139, 0.20: 108, 0.10: 52}
 
 
 def sweep_workload(keep: float) -> Workload:
-    return Workload(f"cfg4_n64k_keep{int(round(keep * 100))}", (65536,), 32, 8, seed=0,
+    return Workload(f"n64k_keep{int(round(keep * 100))}", (65536,), 32, 8, seed=0,
                     k_start=(SWEEP_N64K[keep],), mu=0.5, alpha=0.7, n_init=1, n_window=2)
 
 
@@ -100,7 +100,7 @@ FP8_ALPHAS = tuple([1.0] * 5 + [0.7] * 31)
 
 
 def fp8_workload(layer: int) -> Workload:
-    return Workload(f"cfg5_fp8_varlen_layer{layer}", FP8_SEQLENS, 32, 8, seed=layer,
+    return Workload(f"fp8_varlen_128k_layer{layer}", FP8_SEQLENS, 32, 8, seed=layer,
                     k_start=FP8_KSTART, mu=0.5, alpha=FP8_ALPHAS[layer],
                     n_init=1, n_window=2, fp8=True)
 

@@ -44,11 +44,11 @@ def best_kstart(nb, target, mu, alpha, n_init, n_window):
 def main():
     mu, n_init, n_window = 0.5, 1, 2
     out = {
-        "cfg2_n32k": [best_kstart(256, 0.25, mu, 0.7, n_init, n_window)],
-        "cfg3_n128k": [best_kstart(1024, 0.25, mu, 0.7, n_init, n_window)],
-        "cfg4_n64k": {str(t): best_kstart(512, t, mu, 0.7, n_init, n_window)
+        "n32k_32q8kv": [best_kstart(256, 0.25, mu, 0.7, n_init, n_window)],
+        "n128k_32q8kv": [best_kstart(1024, 0.25, mu, 0.7, n_init, n_window)],
+        "n64k_sweep": {str(t): best_kstart(512, t, mu, 0.7, n_init, n_window)
                       for t in (1.0, 0.5, 0.25, 0.2, 0.1)},
-        "cfg5_fp8": [best_kstart(L // 128, 0.25, mu, 0.7, n_init, n_window)
+        "fp8_varlen_128k": [best_kstart(L // 128, 0.25, mu, 0.7, n_init, n_window)
                      for L in (8192, 16384, 32768, 73728)],
     }
     path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "kstart.json")

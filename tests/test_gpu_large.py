@@ -129,7 +129,7 @@ def _run(w, fp8):
     return res
 
 
-@pytest.fixture(scope="module", params=["cfg2_n32k", "cfg3_n128k", "fp8_layer5"])
+@pytest.fixture(scope="module", params=["n32k_32q8kv", "n128k_32q8kv", "fp8_layer5"])
 def big(request):
     if request.param == "fp8_layer5":
         return _run(S.fp8_workload(5), fp8=True)

@@ -31,25 +31,25 @@ def _oracle_scores(qf, kf, vf, w_cu, Hq, Hkv, beta=0.2, chunk=2048):
 # --------------------------------------------------------------- config 1 ----
 
 @pytest.fixture(scope="module")
-def cfg1():
-    w = S.CONFIGS["cfg1_n2k"]
+def n2k():
+    w = S.CONFIGS["n2k_2q1kv"]
     q, k, v = S.make_workload_qkv(w)
-    note(f"[cfg1] T={w.total_tokens} Hq={w.num_q_heads} Hkv={w.num_kv_heads}")
+    note(f"[n2k] T={w.total_tokens} Hq={w.num_q_heads} Hkv={w.num_kv_heads}")
     return w, (q, k, v), [f64(t) for t in (q, k, v)]
 
 
-def test_cfg1_scores(cfg1):
-    w, (q, k, v), (qf, kf, vf) = cfg1
+def test_n2k_scores(n2k):
+    w, (q, k, v), (qf, kf, vf) = n2k
     p = stem.Problem(w.cu_seqlens, w.num_q_heads, w.num_kv_heads)
     qd, kd, vd = to_dev(q, k, v)
     s = stem.stem_score(p, qd, kd, vd, w.stride, w.chunk_size, w.norm, w.beta)
     torch.cuda.synchronize()
     ref = _oracle_scores(qf, kf, vf, w.cu_seqlens, w.num_q_heads, w.num_kv_heads, w.beta)
-    check_scores(s.cpu().numpy(), ref, "cfg1")
+    check_scores(s.cpu().numpy(), ref, "n2k")
 
 
-def test_cfg1_topk_both_ways(cfg1):
-    w, (q, k, v), (qf, kf, vf) = cfg1
+def test_n2k_topk_both_ways(n2k):
+    w, (q, k, v), (qf, kf, vf) = n2k
     p = stem.Problem(w.cu_seqlens, w.num_q_heads, w.num_kv_heads)
     qd, kd, vd = to_dev(q, k, v)
     s_gpu = stem.stem_score(p, qd, kd, vd, w.stride, w.chunk_size, w.norm, w.beta)
@@ -68,8 +68,8 @@ def test_cfg1_topk_both_ways(cfg1):
     assert int(rc.sum()) == 2 * 71
 
 
-def test_cfg1_bsa_and_dense_bf16(cfg1):
-    w, (q, k, v), (qf, kf, vf) = cfg1
+def test_n2k_bsa_and_dense_bf16(n2k):
+    w, (q, k, v), (qf, kf, vf) = n2k
     p = stem.Problem(w.cu_seqlens, w.num_q_heads, w.num_kv_heads)
     qd, kd, vd = to_dev(q, k, v)
     s_ref = _oracle_scores(qf, kf, vf, w.cu_seqlens, w.num_q_heads, w.num_kv_heads, w.beta)
@@ -78,18 +78,18 @@ def test_cfg1_bsa_and_dense_bf16(cfg1):
     out, lse = stem.stem_bsa_prefill(p, qd, kd, vd, torch.from_numpy(ri).to(dev()),
                                      torch.from_numpy(rc).to(dev()), SCALE, want_lse=True)
     ro, rl = O.block_sparse_attention(qf, kf, vf, ri, rc, w.cu_seqlens, 2, 1, SCALE)
-    check_out(f64(out), ro, BF16_MAX_ABS, BF16_MEAN_REL, "cfg1 bsa")
-    check_lse(lse.cpu().numpy().astype(np.float64), rl, "cfg1 bsa")
+    check_out(f64(out), ro, BF16_MAX_ABS, BF16_MEAN_REL, "n2k bsa")
+    check_lse(lse.cpu().numpy().astype(np.float64), rl, "n2k bsa")
     dout, dlse = stem.stem_dense_prefill(p, qd, kd, vd, SCALE, want_lse=True)
     do, dl = O.dense_causal_attention(qf, kf, vf, w.cu_seqlens, 2, 1, SCALE)
-    check_out(f64(dout), do, BF16_MAX_ABS, BF16_MEAN_REL, "cfg1 dense")
-    check_lse(dlse.cpu().numpy().astype(np.float64), dl, "cfg1 dense")
+    check_out(f64(dout), do, BF16_MAX_ABS, BF16_MEAN_REL, "n2k dense")
+    check_lse(dlse.cpu().numpy().astype(np.float64), dl, "n2k dense")
 
 
-def test_full_lists_equal_dense_kernel(cfg1):
+def test_full_lists_equal_dense_kernel(n2k):
     """Listing every causal block through the sparse kernel reproduces the
     dense kernel bit for bit (same tile loop, same order)."""
-    w, (q, k, v), _ = cfg1
+    w, (q, k, v), _ = n2k
     p = stem.Problem(w.cu_seqlens, 2, 1)
     qd, kd, vd = to_dev(q, k, v)
     fi, fc = O.full_lists(w.cu_seqlens, 2)
@@ -379,8 +379,8 @@ def test_q64_parent_lists_match_square_rows(varlen):
     check_out(f64(out), f64(sq), BF16_MAX_ABS, None, "q64 vs square-row kernel")
 
 
-def test_q64_every_block_listed_equals_dense(cfg1):
-    w, (q, k, v), (qf, kf, vf) = cfg1
+def test_q64_every_block_listed_equals_dense(n2k):
+    w, (q, k, v), (qf, kf, vf) = n2k
     cu = w.cu_seqlens
     p = stem.Problem(cu, w.num_q_heads, w.num_kv_heads)
     qd, kd, vd = to_dev(q, k, v)

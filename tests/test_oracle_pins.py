@@ -455,13 +455,13 @@ def test_kstart_table_matches_derivation_script():
     """The k_start values in stem_synth were written by the committed script
     tests/golden/derive_kstart.py, which calls the oracle only."""
     g = json.load(open(os.path.join(GOLDEN, "kstart.json")))
-    assert tuple(g["cfg2_n32k"]) == S.CONFIGS["cfg2_n32k"].k_start
-    assert tuple(g["cfg3_n128k"]) == S.CONFIGS["cfg3_n128k"].k_start
-    assert {float(k): v for k, v in g["cfg4_n64k"].items()} == S.SWEEP_N64K
-    assert tuple(g["cfg5_fp8"]) == S.FP8_KSTART
+    assert tuple(g["n32k_32q8kv"]) == S.CONFIGS["n32k_32q8kv"].k_start
+    assert tuple(g["n128k_32q8kv"]) == S.CONFIGS["n128k_32q8kv"].k_start
+    assert {float(k): v for k, v in g["n64k_sweep"].items()} == S.SWEEP_N64K
+    assert tuple(g["fp8_varlen_128k"]) == S.FP8_KSTART
 
 
-def test_cfg1_budget_sequence():
+def test_n2k_budget_sequence():
     """Config 1 (k_start 8 of 16 blocks, mu 0.5, alpha 1): the decay from 8 to
     mu*8 = 4 over 16 blocks, and the forced sink + window counted inside."""
     ks = [O.tpd_budget(I, 16, 8, 0.5, 1.0) for I in range(16)]
