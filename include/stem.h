@@ -10,7 +10,9 @@
  *   stem_bsa_prefill    causal block-sparse flash attention over those lists
  *                       (bf16, or fp8 e4m3 with per-block scales).
  * plus stem_dense_prefill, the library's own dense causal attention (the
- * baseline every speed-up is measured against).
+ * baseline every speed-up is measured against), and two variants of stage 3:
+ * stem_bsa_prefill_paged (fp8 K/V in a page pool addressed by a block table)
+ * and stem_bsa_prefill_q64 (lists over 64-query rows against 128-key blocks).
  *
  * Sources: AngelSlim documentation "Stem: Rethinking Causal Information Flow in
  * Sparse Attention" (features/sparse_attention/stem.md) §2.1-2.3 and the §6
@@ -94,8 +96,9 @@ const char *stem_status_string(int status);
  *   l_J = ln max_{t in key block J} ||V[t][g]||^2, mean and population std
  *   taken over the nb_z key blocks of sequence z.
  * S is fp32 [Hq][R][max_nb]; every entry with J > I or J >= nb_z is -inf.
- * q, k, v: bf16.  stride divides block_size; chunk_size is a positive
- * multiple of block_size (it orders the work, it changes no value).
+ * q, k, v: bf16.  stride must divide block_size (else INVALID_ARG); stride 8
+ * is the one implemented (others return UNSUPPORTED).  chunk_size is a
+ * positive multiple of block_size (it orders the work, it changes no value).
  * workspace: device memory of at least stem_score_workspace_bytes(p) bytes,
  * 256-byte aligned; its contents on return are unspecified.
  * ------------------------------------------------------------------------- */
@@ -170,7 +173,9 @@ size_t stem_attn_workspace_bytes(const stem_problem_t *p, int32_t dtype);
  * Precision: Q.K^T in the input type (bf16, or e4m3 with fp32 scales), fp32
  * accumulation and softmax; P.V with P rounded to fp16 against an exact fp16
  * copy of V for bf16 inputs (V magnitudes above 65504 saturate), and to e4m3
- * (as p * 256) for fp8 inputs except in the diagonal block, which uses fp16.
+ * for fp8 inputs (each weight times the block's V scale, relative to a running
+ * reference that keeps the largest weight between 152 and 430, below e4m3's
+ * 448), except in the diagonal block, which uses fp16.
  * ------------------------------------------------------------------------- */
 int stem_bsa_prefill(const stem_problem_t *p, int32_t dtype, const void *q, const void *k,
                      const void *v, const float *q_scale, const float *k_scale,
