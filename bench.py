@@ -390,10 +390,13 @@ def fp8_varlen(args, torch, stem, S, dev):
         log(f"[bench]   fp8 {tag}: layer {t_layer:.2f} ms (bsa {timer.mean('bsa'):.2f} ms, "
             f"rho {pairs / dense_pairs:.4f})")
     idx, cnt = lists["alpha_0.7"]
-    dtimer = StageTimer(torch, ["dense", "paged"])
+    dtimer = StageTimer(torch, ["dense", "paged", "e4m3_weights", "fp16_weights"])
     dfn = [lambda: stem.stem_dense_prefill(p, qa, ka, va, scales=scl, out=out, workspace=aws),
            lambda: stem.stem_bsa_prefill_paged(p, qa, kpd, vpd, tabd, idx, cnt, scales=pscl, out=out,
-                                               workspace=aws)]
+                                               workspace=aws),
+           lambda: stem.stem_bsa_prefill(p, qa, ka, va, idx, cnt, scales=scl, out=out, workspace=aws),
+           lambda: stem.stem_bsa_prefill(p, qa, ka, va, idx, cnt, scales=scl, out=out, workspace=aws,
+                                         fp16_weights=True)]
     dtimer.run(dfn)
     torch.cuda.synchronize()
     devs = [dtimer.run(dfn) for _ in range(3)]
@@ -407,6 +410,12 @@ def fp8_varlen(args, torch, stem, S, dev):
     lo["paged_vs_contiguous"] = t_paged / lo["stages_ms"]["bsa"]
     log(f"[bench]   fp8 alpha_0.7 paged ({kpd.shape[0]} shuffled pages): bsa {t_paged:.2f} ms "
         f"({lo['paged_vs_contiguous']:.3f}x contiguous)")
+    # P.V with fp16 weights (the accurate mode for peaked attention), timed
+    # alternately with the e4m3-weight call on the same lists
+    lo["fp16_weights_bsa_ms"] = dtimer.mean("fp16_weights")
+    lo["fp16_weights_vs_e4m3_weights"] = dtimer.mean("fp16_weights") / dtimer.mean("e4m3_weights")
+    log(f"[bench]   fp8 alpha_0.7 with fp16 weights for P.V: bsa {dtimer.mean('fp16_weights'):.2f} ms "
+        f"({lo['fp16_weights_vs_e4m3_weights']:.3f}x the e4m3-weight call, timed alternately)")
     for L_ in layers.values():
         L_["skip_overhead"] = L_["stages_ms"]["bsa"] / (L_["computed_pair_fraction"] * t_dense) - 1.0
     total = 5 * layers["alpha_1.0"]["ms"] + 31 * lo["ms"]

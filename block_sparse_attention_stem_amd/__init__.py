@@ -27,6 +27,7 @@ LIB_PATH = os.path.join(_PKG, "libstem.so")
 STEM_OK = 0
 STEM_DTYPE_BF16 = 0
 STEM_DTYPE_FP8_E4M3 = 1
+STEM_DTYPE_FP8_E4M3_PV16 = 2     # e4m3 inputs, P.V with fp16 weights
 STATUS = {0: "STEM_OK", 1: "STEM_ERR_INVALID_ARG", 2: "STEM_ERR_UNSUPPORTED",
           3: "STEM_ERR_CAPACITY", 4: "STEM_ERR_WORKSPACE", 5: "STEM_ERR_HIP"}
 
@@ -203,15 +204,17 @@ def stem_schedule_topk(p: Problem, scores: torch.Tensor, k_start, mu: float, alp
     return block_idx, block_cnt
 
 
-def _attn_inputs(p: Problem, q, k, v, scales):
+def _attn_inputs(p: Problem, q, k, v, scales, fp16_weights: bool = False):
     if q.dtype == torch.bfloat16:
         dt = STEM_DTYPE_BF16
         for name, t, h in (("q", q, p.Hq), ("k", k, p.Hkv), ("v", v, p.Hkv)):
             _need(t, name, torch.bfloat16, (p.T, h, p.d))
         if scales is not None:
             raise ValueError("bf16 attention takes no scales")
+        if fp16_weights:
+            raise ValueError("fp16_weights applies to e4m3 inputs only")
         return dt, (None, None, None)
-    dt = STEM_DTYPE_FP8_E4M3
+    dt = STEM_DTYPE_FP8_E4M3_PV16 if fp16_weights else STEM_DTYPE_FP8_E4M3
     for name, t, h in (("q", q, p.Hq), ("k", k, p.Hkv), ("v", v, p.Hkv)):
         if t.dtype == torch.float8_e4m3fn:
             t = t.view(torch.uint8)
@@ -240,10 +243,13 @@ def _attn_workspace(p: Problem, dt: int, workspace, device):
 
 def stem_bsa_prefill(p: Problem, q, k, v, block_idx, block_cnt, softmax_scale: Optional[float] = None,
                      scales=None, out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                     want_lse: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
-    """Causal block-sparse attention over the lists: out bf16 [T][Hq][d] (+ lse fp32 [Hq][T])."""
+                     want_lse: bool = False, workspace: Optional[torch.Tensor] = None, stream=None,
+                     fp16_weights: bool = False):
+    """Causal block-sparse attention over the lists: out bf16 [T][Hq][d] (+ lse fp32 [Hq][T]).
+
+    fp16_weights (e4m3 inputs only): P.V with fp16 instead of e4m3 weights."""
     lib = load_library()
-    dt, (qs, kss, vs) = _attn_inputs(p, q, k, v, scales)
+    dt, (qs, kss, vs) = _attn_inputs(p, q, k, v, scales, fp16_weights)
     _need(block_cnt, "block_cnt", torch.int32, (p.Hq, p.R))
     if block_idx.dtype != torch.int32 or block_idx.dim() != 3 or tuple(block_idx.shape[:2]) != (p.Hq, p.R) \
             or not block_idx.is_contiguous():
@@ -344,10 +350,11 @@ def stem_bsa_prefill_paged(p: Problem, q, k_pages, v_pages, block_table, block_i
 
 def stem_dense_prefill(p: Problem, q, k, v, softmax_scale: Optional[float] = None, scales=None,
                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                       want_lse: bool = False, workspace: Optional[torch.Tensor] = None, stream=None):
-    """Dense causal attention with the same tile kernel."""
+                       want_lse: bool = False, workspace: Optional[torch.Tensor] = None, stream=None,
+                       fp16_weights: bool = False):
+    """Dense causal attention with the same tile kernel (fp16_weights as in stem_bsa_prefill)."""
     lib = load_library()
-    dt, (qs, kss, vs) = _attn_inputs(p, q, k, v, scales)
+    dt, (qs, kss, vs) = _attn_inputs(p, q, k, v, scales, fp16_weights)
     scale = 1.0 / math.sqrt(p.d) if softmax_scale is None else float(softmax_scale)
     if out is None:
         out = torch.empty((p.T, p.Hq, p.d), dtype=torch.bfloat16, device=q.device)

@@ -687,23 +687,26 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
 
 // ====================================================================== fp8
 // Same pipeline on e4m3 operands with the 32x32x64 fp8 MFMA: Q.K^T in two
-// K=64 steps per key tile, P quantised to e4m3 (at most 256 < 448, see
+// K=64 steps per key tile, P quantised to e4m3 (at most 430 < 448, see
 // softmax_fp8), P.V in two K=64 steps per head-dim tile.  Per-block scales:
 // the q and k scales fold into the exponent scale c of the block, the v
 // scale into the exponent offset of the weights (softmax_fp8), so no
 // per-element multiply is spent on either.  The diagonal block, where the
 // first queries of a sequence see only a few keys and 3-bit weights would not
-// average out, runs its P.V in fp16 from the exact fp16 V^T image.
+// average out, runs its P.V in fp16 from the exact fp16 V^T image.  kPV16
+// runs every block's P.V that way (fp16 weights, 11 significant bits): the
+// e4m3 V^T tile is then never loaded, and a row whose attention sits on a few
+// keys keeps bf16-level accuracy, at the price of twice the P.V MFMA time.
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
   uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0u, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
 
-template <bool kSparse>
+template <bool kSparse, bool kPV16>
 __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable t, int rows) {
   __shared__ __attribute__((aligned(1024))) uint8_t Ks[kTile8];      // e4m3 K, [key][d], padded rows
-  __shared__ __attribute__((aligned(1024))) uint8_t Vs[kTile8];      // e4m3 V^T image, padded rows
+  __shared__ __attribute__((aligned(1024))) uint8_t Vs[kTile8];      // e4m3 V^T image (unused with kPV16)
   __shared__ __attribute__((aligned(1024))) uint16_t Vh[kTile16];    // fp16 V^T image (diagonal)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -801,7 +804,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
   // block may be the diagonal one (only the last listed block can be).
   enum { kNone = 0, kV8 = 1, kV16 = 2 };
   auto step = [&](int J, int Jn, int kNext, bool may_diag, bool v16_pending) __attribute__((always_inline)) {
-    if (v16_pending) wait_vmcnt<8>(); else wait_vmcnt<4>();
+    if (kPV16 || v16_pending) wait_vmcnt<8>(); else wait_vmcnt<4>();
     block_sync();
     const bool diag = may_diag && (J == w.I);
     const int sr = zrow + J;
@@ -819,7 +822,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
     wait_vmcnt<0>();
     block_sync();
     if (kNext != kNone) issue_k(Jn);
-    if (!diag) {
+    if (!kPV16 && !diag) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         i32x8 pk;
@@ -847,8 +850,8 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
       }
     }
     block_sync();
-    if (kNext == kV8) issue_v8(Jn);
-    if (kNext == kV16) issue_v16(Jn);
+    if (kNext == kV8 && !kPV16) issue_v8(Jn);
+    if (kNext == kV16 || (kNext == kV8 && kPV16)) issue_v16(Jn);
   };
 
   // Lists are ascending, so only the last block can be the diagonal one: the
@@ -857,7 +860,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
   int J = kSparse ? clampJ(list[0]) : 0;
   const bool first_v16 = (n_blk == 1) && (J == w.I);
   issue_k(J);
-  if (first_v16) issue_v16(J); else issue_v8(J);
+  if (first_v16 || kPV16) issue_v16(J); else issue_v8(J);
   for (int b = 0; b + 2 < n_blk; ++b) {
     const int Jn = kSparse ? clampJ(list[b + 1]) : b + 1;
     step(J, Jn, kV8, false, false);
@@ -912,12 +915,15 @@ hipError_t launch_vprep_paged(const AttnLaunch &a, const SeqTable &t, int rows, 
   return hipGetLastError();
 }
 
-hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows, bool sparse, bool fp8,
+hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows, bool sparse, bool fp8, bool pv16,
                        hipStream_t s) {
   const dim3 grid(rows * a.Hq);
-  if (fp8) {
-    if (sparse) hipLaunchKernelGGL(attn_fp8_kernel<true>, grid, dim3(256), 0, s, a, t, rows);
-    else hipLaunchKernelGGL(attn_fp8_kernel<false>, grid, dim3(256), 0, s, a, t, rows);
+  if (fp8 && pv16) {
+    if (sparse) hipLaunchKernelGGL((attn_fp8_kernel<true, true>), grid, dim3(256), 0, s, a, t, rows);
+    else hipLaunchKernelGGL((attn_fp8_kernel<false, true>), grid, dim3(256), 0, s, a, t, rows);
+  } else if (fp8) {
+    if (sparse) hipLaunchKernelGGL((attn_fp8_kernel<true, false>), grid, dim3(256), 0, s, a, t, rows);
+    else hipLaunchKernelGGL((attn_fp8_kernel<false, false>), grid, dim3(256), 0, s, a, t, rows);
   } else {
     if (sparse) hipLaunchKernelGGL((attn_bf16_kernel<true, false>), grid, dim3(512), 0, s, a, t, rows);
     else hipLaunchKernelGGL((attn_bf16_kernel<false, false>), grid, dim3(512), 0, s, a, t, rows);

@@ -205,8 +205,8 @@ int stem_schedule_topk(const stem_problem_t *p, const float *scores, const doubl
 size_t stem_attn_workspace_bytes(const stem_problem_t *p, int32_t dtype) {
   Shape s;
   if (check_problem(p, &s) != STEM_OK) return 0;
-  if (dtype != STEM_DTYPE_BF16 && dtype != STEM_DTYPE_FP8_E4M3) return 0;
-  return attn_workspace_bytes(s.Hkv, s.R, dtype == STEM_DTYPE_FP8_E4M3);
+  if (dtype != STEM_DTYPE_BF16 && dtype != STEM_DTYPE_FP8_E4M3 && dtype != STEM_DTYPE_FP8_E4M3_PV16) return 0;
+  return attn_workspace_bytes(s.Hkv, s.R, dtype != STEM_DTYPE_BF16);
 }
 
 static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, const void *k,
@@ -221,13 +221,14 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
   if (st != STEM_OK) return st;
   if (!q || !k || !v || !out) return STEM_ERR_INVALID_ARG;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return STEM_ERR_INVALID_ARG;
-  bool fp8;
+  bool fp8, pv16 = false;
   if (dtype == STEM_DTYPE_BF16) {
     if (q_scale || k_scale || v_scale) return STEM_ERR_INVALID_ARG;
     fp8 = false;
-  } else if (dtype == STEM_DTYPE_FP8_E4M3) {
+  } else if (dtype == STEM_DTYPE_FP8_E4M3 || dtype == STEM_DTYPE_FP8_E4M3_PV16) {
     if (!q_scale || !k_scale || !v_scale) return STEM_ERR_INVALID_ARG;
     fp8 = true;
+    pv16 = dtype == STEM_DTYPE_FP8_E4M3_PV16;
   } else {
     return STEM_ERR_UNSUPPORTED;
   }
@@ -282,7 +283,7 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
     const int rows = t.row[n] - t.row[0];
     if ((int64_t)rows * s.Hq >= ((int64_t)1 << 31)) return STEM_ERR_UNSUPPORTED;
     if (table && launch_vprep_paged(a, t, rows, hs) != hipSuccess) return STEM_ERR_HIP;
-    const hipError_t e = q64 ? launch_attn_q64(a, t, rows, hs) : launch_attn(a, t, rows, sparse, fp8, hs);
+    const hipError_t e = q64 ? launch_attn_q64(a, t, rows, hs) : launch_attn(a, t, rows, sparse, fp8, pv16, hs);
     if (e != hipSuccess) return STEM_ERR_HIP;
   }
   return STEM_OK;

@@ -154,8 +154,9 @@ size_t attn_workspace_scales_offset(int Hkv, int R);
 hipError_t launch_vprep(const AttnLaunch &a, bool fp8, hipStream_t s);
 // Paged pre-pass for the rows of one launch's sequences.
 hipError_t launch_vprep_paged(const AttnLaunch &a, const SeqTable &t, int rows_in_launch, hipStream_t s);
+// pv16 (fp8 only): every block's P.V with fp16 weights against the fp16 V^T image.
 hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows_in_launch,
-                       bool sparse, bool fp8, hipStream_t s);
+                       bool sparse, bool fp8, bool pv16, hipStream_t s);
 // bf16 block-sparse attention over 64-query rows (lists [Hq][2R][k_cap]).
 hipError_t launch_attn_q64(const AttnLaunch &a, const SeqTable &t, int rows_in_launch, hipStream_t s);
 

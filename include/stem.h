@@ -61,7 +61,8 @@ typedef enum {
 
 typedef enum {
   STEM_DTYPE_BF16 = 0,        /* bfloat16 Q/K/V                              */
-  STEM_DTYPE_FP8_E4M3 = 1     /* OCP e4m3fn codes with fp32 per-block scales  */
+  STEM_DTYPE_FP8_E4M3 = 1,    /* OCP e4m3fn codes with fp32 per-block scales  */
+  STEM_DTYPE_FP8_E4M3_PV16 = 2 /* the same inputs; P.V with fp16 weights     */
 } stem_dtype_t;
 
 /* One packed batch of sequences (the shape of the problem). */
@@ -152,7 +153,7 @@ int32_t stem_max_kept(const stem_problem_t *p, const double *k_start_host, doubl
  * Contents on return are unspecified; concurrent calls need separate
  * workspaces.
  * ------------------------------------------------------------------------- */
-size_t stem_attn_workspace_bytes(const stem_problem_t *p, int32_t dtype);
+size_t stem_attn_workspace_bytes(const stem_problem_t *p, int32_t dtype);   /* FP8_E4M3_PV16: as fp8 */
 
 /* ---------------------------------------------------------------------------
  * Stage 3: causal block-sparse attention.  AngelSlim doc §2.3: exact
@@ -183,6 +184,19 @@ int stem_bsa_prefill(const stem_problem_t *p, int32_t dtype, const void *q, cons
                      const int32_t *block_cnt, int32_t k_cap, float softmax_scale,
                      void *out, float *lse, void *workspace, size_t workspace_bytes,
                      void *stream);
+
+/* dtype FP8_E4M3_PV16 takes the FP8_E4M3 inputs and scales but runs every
+ * block's P.V like the diagonal block's: fp16 weights against the exact fp16
+ * V^T image.  The e4m3 weight rounding (relative error up to 2^-4 per weight)
+ * averages out when attention is spread over many keys, but not when a few
+ * keys hold it; this dtype keeps such rows at bf16-level output error, for
+ * about 1.25x the e4m3 time.  Q.K^T stays e4m3 in both: the fp8 MFMA sums its
+ * 64 products per step with less than fp32 precision (measured error up to
+ * 2^-15 of the sum of |products| on quantised Gaussian data), which shows in
+ * the LSE of very large logits.  Taken by stem_bsa_prefill and
+ * stem_dense_prefill (the paged and 64-query entry points have no dtype
+ * argument and no such mode).
+ * ------------------------------------------------------------------------- */
 
 /* ---------------------------------------------------------------------------
  * Dense causal attention with the same tile kernel (every causal block).

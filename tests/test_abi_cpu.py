@@ -7,6 +7,7 @@ import os
 import re
 
 import pytest
+import torch
 
 import block_sparse_attention_stem_amd as stem
 import oracle as O
@@ -135,9 +136,18 @@ def test_attention_argument_errors():
     assert lib.stem_dense_prefill(p.ref, 0, None, f, f, None, None, None, 0.1, f, None, f, W, None) == 1
     assert lib.stem_dense_prefill(p.ref, 0, f, f, f, None, None, None, 0.1, f, None, ctypes.c_void_p(0x1010),
                                   W, None) == 4
+    # dtype 2 (e4m3 inputs, fp16 weights for P.V) needs the fp8 scales and workspace too
+    assert lib.stem_bsa_prefill(p.ref, 2, f, f, f, None, None, None, f, f, 8, 0.1, f, None, f, W, None) == 1
+    assert lib.stem_dense_prefill(p.ref, 2, f, f, f, f, f, f, 0.1, f, None, f, 100, None) == 4
+    assert lib.stem_dense_prefill(p.ref, 3, f, f, f, f, f, f, 0.1, f, None, f, W, None) == 2
     assert stem.stem_attn_workspace_bytes(p, 0) == 1024 * 2 * 272
     assert stem.stem_attn_workspace_bytes(p, 1) == 1024 * 2 * 416 + (1024 // 128) * 2 * 8
+    assert stem.stem_attn_workspace_bytes(p, 2) == stem.stem_attn_workspace_bytes(p, 1)
     assert stem.stem_attn_workspace_bytes(p, 5) == 0
+    with pytest.raises(ValueError):
+        stem.stem_dense_prefill(p, torch.zeros(1024, 4, 128, dtype=torch.bfloat16),
+                                torch.zeros(1024, 2, 128, dtype=torch.bfloat16),
+                                torch.zeros(1024, 2, 128, dtype=torch.bfloat16), fp16_weights=True)
 
 
 def test_paged_attention_argument_errors():

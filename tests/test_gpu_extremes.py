@@ -9,7 +9,9 @@ rounded to e4m3 before P.V (3 mantissa bits, relative error at most 2^-4) and
 the row sum uses the unrounded weights, so the output error is bounded by
 2^-4 * max|v| over the row's keys, which the flat logits of the workload
 inputs average far below the 6e-2 bar but peaked logits do not; those cases
-are checked against that bound.
+are checked against that bound.  With fp16_weights (dtype FP8_E4M3_PV16) every
+block's P.V uses fp16 weights, and e4m3 inputs meet the bf16 output bar on
+the same peaked logits.
 """
 import math
 
@@ -158,3 +160,32 @@ def test_fp8_block_maxima_ramps(slope):
     q, k, v = _ramp(slope)
     idx, cnt = _lists("all", S.cu_from_lengths(LENS))
     _run_fp8(q, k, v, idx, cnt, f"fp8 ramp {slope:+.0f}", peaked=True)
+
+
+@pytest.mark.parametrize("gain", [1, 2, 4])
+def test_fp8_fp16_weights_meet_the_bf16_bar_on_peaked_logits(gain):
+    """e4m3 Q/K/V with fp16 weights for P.V: the output bar of the bf16 path.
+    The LSE is checked up to gain 2: Q.K^T stays on the fp8 MFMA, whose sums
+    carry an error of up to about 2^-15 of the sum of |products|, i.e. a few
+    1e-3 nats once logits reach +-60 (gain 4)."""
+    q, k, v = _scaled(gain)
+    cu = S.cu_from_lengths(LENS)
+    p = stem.Problem(cu, HQ, HKV)
+    idx, cnt = _lists("random", cu)
+    (q8, k8, v8), (qs, ks, vs) = quantize_fp8(q, k, v, LENS)
+    qf, kf, vf = dequant(q8, qs), dequant(k8, ks), dequant(v8, vs)
+    sc = to_dev(qs, ks, vs)
+    out, lse = stem.stem_bsa_prefill(p, *to_dev(q8, k8, v8), torch.from_numpy(idx).to(dev()),
+                                     torch.from_numpy(cnt).to(dev()), SCALE, scales=sc, want_lse=True,
+                                     fp16_weights=True)
+    ro, rl = O.block_sparse_attention(qf, kf, vf, idx, cnt, cu, HQ, HKV, SCALE)
+    check_out(f64(out), ro, BF16_MAX_ABS, BF16_MEAN_REL, f"fp8/fp16-weights gain {gain} bsa")
+    if gain <= 2:
+        check_lse(lse.cpu().numpy().astype(np.float64), rl, f"fp8/fp16-weights gain {gain}")
+    dout = stem.stem_dense_prefill(p, *to_dev(q8, k8, v8), SCALE, scales=sc, fp16_weights=True)
+    do, _ = O.dense_causal_attention(qf, kf, vf, cu, HQ, HKV, SCALE)
+    check_out(f64(dout), do, BF16_MAX_ABS, BF16_MEAN_REL, f"fp8/fp16-weights gain {gain} dense")
+    fi, fc = O.full_lists(cu, HQ)
+    full = stem.stem_bsa_prefill(p, *to_dev(q8, k8, v8), torch.from_numpy(fi).to(dev()),
+                                 torch.from_numpy(fc).to(dev()), SCALE, scales=sc, fp16_weights=True)
+    assert torch.equal(full, dout), "every block listed must equal the dense call"

@@ -1,5 +1,5 @@
 """GPU parity on seeded random problem shapes: the whole path (scores, lists,
-bf16 / fp8 / paged / 64x128 attention) against the oracle, over random
+bf16 / fp8 / fp8 with fp16 weights / paged / 64x128 attention) against the oracle, over random
 sequence counts and lengths, head ratios and schedule parameters.  Each
 case is deterministic (its seed fixes every draw) and small enough for the
 oracle to check every output."""
@@ -81,3 +81,5 @@ def test_random_shapes_whole_path(seed):
     op, lp = stem.stem_bsa_prefill_paged(p, qa, kpd, vpd, tabd, idx, cnt, scale, scales=to_dev(qs, ksp, vsp),
                                          want_lse=True)
     assert torch.equal(op, o8) and torch.equal(lp, l8), f"random {seed}: paged differs from contiguous"
+    o16 = stem.stem_bsa_prefill(p, qa, ka, va, idx, cnt, scale, scales=scl, fp16_weights=True)
+    check_out(f64(o16), ro8, BF16_MAX_ABS, BF16_MEAN_REL, f"random {seed} fp8 inputs, fp16 weights")
