@@ -169,6 +169,24 @@ __device__ __forceinline__ void score_static_for(F &&f) {
   score_static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Max over each row of 16 lanes, left in every lane of the row: four DPP
+// steps (pairs, quads, half-row mirror, row mirror) fused into the max, no
+// LDS round trip.
+__device__ __forceinline__ float dpp_max16(float x) {
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, true)));
+  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, true)));
+  return x;
+}
+// Max of lanes l and l ^ 32, in every lane: v_permlane32_swap with the value
+// as both operands returns lane l's and lane l ^ 32's values, in some order.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)__float_as_int(x), (unsigned)__float_as_int(x), false,
+                                                  false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+
 __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, int n_items) {
   __shared__ __attribute__((aligned(1024))) uint16_t A0[kTileS * kScoreBK];
   __shared__ __attribute__((aligned(1024))) uint16_t A1[kTileS * kScoreBK];
@@ -327,13 +345,8 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
         if (diag && j > i) x = -INFINITY;
         if (r < 8) m0 = fmaxf(m0, x); else m1 = fmaxf(m1, x);
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        m0 = fmaxf(m0, __shfl_xor(m0, o, 64));
-        m1 = fmaxf(m1, __shfl_xor(m1, o, 64));
-      }
-      m0 = fmaxf(m0, __shfl_xor(m0, 32, 64));
-      m1 = fmaxf(m1, __shfl_xor(m1, 32, 64));
+      m0 = max_xor32(dpp_max16(m0));
+      m1 = max_xor32(dpp_max16(m1));
       if ((lane & 15) == 0 && lane < 32) {
         const int J = jb / 16 + (lane >> 4);
         const int I0 = ib / 16;

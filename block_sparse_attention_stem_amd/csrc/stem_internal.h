@@ -66,7 +66,7 @@ __device__ __forceinline__ int xcd_chunk_item(int b, int n_items) {
   return (b & 7) * per + (b >> 3);
 }
 
-// Token-Position-Decay budget// Token-Position-Decay budget: k(I) = floor(ke - ke (1 - mu) I / nb), with
+// Token-Position-Decay budget: k(I) = floor(ke - ke (1 - mu) I / nb), with
 // ke = alpha * k_start already folded in.  Evaluated in fp64 without
 // contraction; the 1e-9 nudge absorbs the rounding of the fp64 steps when the
 // exact (decimal) value is an integer.
