@@ -169,22 +169,40 @@ __device__ __forceinline__ void score_static_for(F &&f) {
   score_static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Max over each row of 16 lanes, left in every lane of the row: four DPP
-// steps (pairs, quads, half-row mirror, row mirror) fused into the max, no
-// LDS round trip.
-__device__ __forceinline__ float dpp_max16(float x) {
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, true)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, true)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, true)));
-  x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, true)));
-  return x;
+// Cross-lane max-pool on an order-preserving integer image of the floats:
+// for non-NaN x, key(x) = bits ^ ((bits >> 31) & 0x7fffffff) orders like x as
+// a signed integer and is its own inverse.  Integer max needs no IEEE
+// canonicalisation, so each DPP step folds into one v_max_i32.
+__device__ __forceinline__ int max_key(float x) {
+  const int b = __float_as_int(x);
+  return b ^ ((b >> 31) & 0x7fffffff);
 }
-// Max of lanes l and l ^ 32, in every lane: v_permlane32_swap with the value
-// as both operands returns lane l's and lane l ^ 32's values, in some order.
-__device__ __forceinline__ float max_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap((unsigned)__float_as_int(x), (unsigned)__float_as_int(x), false,
-                                                  false);
-  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+__device__ __forceinline__ float key_max(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7fffffff)); }
+template <int kCtrl>
+__device__ __forceinline__ int dpp_imax(int k) {
+  const int o = __builtin_amdgcn_update_dpp(0, k, kCtrl, 0xF, 0xF, true);
+  return k > o ? k : o;
+}
+// k[n] <- max over its row of 16 lanes (pairs, quads, half-row mirror, row
+// mirror), then over lanes l and l ^ 32 (v_permlane32_swap with the value as
+// both operands returns both halves' values).  The N chains advance one step
+// at a time, so no DPP read waits on the write just before it.
+template <int N>
+__device__ __forceinline__ void key_max_rows_and_halves(int (&k)[N]) {
+#pragma unroll
+  for (int n = 0; n < N; ++n) k[n] = dpp_imax<0xB1>(k[n]);
+#pragma unroll
+  for (int n = 0; n < N; ++n) k[n] = dpp_imax<0x4E>(k[n]);
+#pragma unroll
+  for (int n = 0; n < N; ++n) k[n] = dpp_imax<0x141>(k[n]);
+#pragma unroll
+  for (int n = 0; n < N; ++n) k[n] = dpp_imax<0x140>(k[n]);
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)k[n], (unsigned)k[n], false, false);
+    const int a = (int)r[0], b = (int)r[1];
+    k[n] = a > b ? a : b;
+  }
 }
 
 __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, int n_items) {
@@ -330,24 +348,42 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
   const bool diag = (ti == tj);
   const size_t srow0 = ((size_t)h * a.R + t.row[z]) * a.max_nb;
   const float *bon = a.bonus + (size_t)g * a.R + t.row[z];
+  if (diag) {
+    // the strided causal mask j <= i (only the diagonal tile crosses it)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < 4; ++nj) {
+        const int ib = ibase + wm * 64 + mi * 32, j = jbase + wn * 128 + nj * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (j > ib + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) acc[mi][nj][r] = -INFINITY;
+      }
+  }
+  // per lane: the max of its 8 rows of each 16-row half, then across lanes
+  int key[16];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+    for (int nj = 0; nj < 4; ++nj) {
+      float m0 = acc[mi][nj][0], m1 = acc[mi][nj][8];
+#pragma unroll
+      for (int r = 1; r < 8; ++r) {
+        m0 = fmaxf(m0, acc[mi][nj][r]);
+        m1 = fmaxf(m1, acc[mi][nj][8 + r]);
+      }
+      key[8 * mi + 2 * nj] = max_key(m0);
+      key[8 * mi + 2 * nj + 1] = max_key(m1);
+    }
+  key_max_rows_and_halves(key);
 #pragma unroll
   for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
     for (int nj = 0; nj < 4; ++nj) {
       const int ib = ibase + wm * 64 + mi * 32;    // strided row base
       const int jb = jbase + wn * 128 + nj * 32;
-      const int j = jb + (lane & 31);
-      float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = ib + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        float x = acc[mi][nj][r];
-        if (diag && j > i) x = -INFINITY;
-        if (r < 8) m0 = fmaxf(m0, x); else m1 = fmaxf(m1, x);
-      }
-      m0 = max_xor32(dpp_max16(m0));
-      m1 = max_xor32(dpp_max16(m1));
       if ((lane & 15) == 0 && lane < 32) {
+        const float m0 = key_max(key[8 * mi + 2 * nj]), m1 = key_max(key[8 * mi + 2 * nj + 1]);
         const int J = jb / 16 + (lane >> 4);
         const int I0 = ib / 16;
         if (J < nb) {
