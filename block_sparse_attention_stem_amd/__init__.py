@@ -375,15 +375,20 @@ def stem_prefill(p: Problem, q, k, v, k_start, mu: float = 0.5, alpha: float = 1
                  n_init: int = DEFAULTS["initial_blocks"], n_window: int = DEFAULTS["window_size"],
                  stride: int = DEFAULTS["stride"], chunk_size: int = DEFAULTS["chunk_size"],
                  norm: float = DEFAULTS["norm"], beta: float = DEFAULTS["beta"],
-                 fp8_inputs=None, softmax_scale: Optional[float] = None, stream=None):
+                 fp8_inputs=None, softmax_scale: Optional[float] = None, stream=None,
+                 fp16_weights: bool = False):
     """The whole path for one layer: score -> schedule/top-k -> block-sparse attention.
 
     Scoring runs on the bf16 q, k, v.  With `fp8_inputs = (q8, k8, v8, (qs, ks, vs))`
-    the attention stage runs on those e4m3 tensors instead.
+    the attention stage runs on those e4m3 tensors instead (with fp16_weights,
+    P.V keeps fp16 weights; see stem_bsa_prefill).
     """
     s = stem_score(p, q, k, v, stride, chunk_size, norm, beta, stream=stream)
     idx, cnt = stem_schedule_topk(p, s, k_start, mu, alpha, n_init, n_window, stream=stream)
     if fp8_inputs is None:
+        if fp16_weights:
+            raise ValueError("fp16_weights applies to fp8_inputs only")
         return stem_bsa_prefill(p, q, k, v, idx, cnt, softmax_scale, stream=stream)
     q8, k8, v8, sc = fp8_inputs
-    return stem_bsa_prefill(p, q8, k8, v8, idx, cnt, softmax_scale, scales=sc, stream=stream)
+    return stem_bsa_prefill(p, q8, k8, v8, idx, cnt, softmax_scale, scales=sc, stream=stream,
+                            fp16_weights=fp16_weights)

@@ -389,3 +389,26 @@ def test_q64_every_block_listed_equals_dense(n2k):
                                     torch.from_numpy(fc).to(dev()), SCALE)
     do, _ = O.dense_causal_attention(qf, kf, vf, cu, w.num_q_heads, w.num_kv_heads, SCALE)
     check_out(f64(out), do, BF16_MAX_ABS, BF16_MEAN_REL, "q64 all blocks vs dense")
+
+
+# ------------------------------------------------------ one-call wrapper ----
+
+def test_stem_prefill_equals_the_three_calls(fp8_small):
+    """stem_prefill (score -> schedule -> attention in one call) gives exactly
+    what the three entry points give, for bf16 and for e4m3 inputs (with e4m3
+    and with fp16 weights for P.V)."""
+    lens, (q, k, v), (q8, k8, v8), (qs, ks, vs), _ = fp8_small
+    cu = S.cu_from_lengths(lens)
+    p = stem.Problem(cu, 4, 2)
+    qd, kd, vd = to_dev(q, k, v)
+    kstart, mu, alpha = [1, 3, 4], 0.5, 0.7
+    s = stem.stem_score(p, qd, kd, vd)
+    idx, cnt = stem.stem_schedule_topk(p, s, kstart, mu, alpha, 1, 2)
+    a = stem.stem_prefill(p, qd, kd, vd, kstart, mu, alpha, n_init=1, n_window=2, softmax_scale=SCALE)
+    assert torch.equal(a, stem.stem_bsa_prefill(p, qd, kd, vd, idx, cnt, SCALE))
+    f8 = to_dev(q8, k8, v8)
+    sc = to_dev(qs, ks, vs)
+    for w16 in (False, True):
+        b = stem.stem_prefill(p, qd, kd, vd, kstart, mu, alpha, n_init=1, n_window=2, softmax_scale=SCALE,
+                              fp8_inputs=(*f8, sc), fp16_weights=w16)
+        assert torch.equal(b, stem.stem_bsa_prefill(p, *f8, idx, cnt, SCALE, scales=sc, fp16_weights=w16))
