@@ -799,9 +799,11 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
 #pragma unroll
   for (int u = 0; u < 4; ++u) o[u] = f32x16{};
 
-  // kNext: what the step prefetches for the next block (0 nothing, 1 the e4m3
-  // V^T image, 2 the fp16 one for a diagonal block); kDiagPath: whether this
-  // block may be the diagonal one (only the last listed block can be).
+  // kNext: what the step prefetches for the next block (kNone nothing, kV8
+  // its V^T image (the fp16 one under kPV16, else the e4m3 one), kV16 the fp16
+  // image of a diagonal block); may_diag: whether this block may be the
+  // diagonal one (only the last listed block can be); v16_pending: its fp16
+  // image was requested last, so the wait at the top leaves it in flight.
   enum { kNone = 0, kV8 = 1, kV16 = 2 };
   auto step = [&](int J, int Jn, int kNext, bool may_diag, bool v16_pending) __attribute__((always_inline)) {
     if (kPV16 || v16_pending) wait_vmcnt<8>(); else wait_vmcnt<4>();
