@@ -8,15 +8,15 @@
  *   stem_schedule_topk  Token-Position-Decay budget per query block, sink and
  *                       window blocks forced, per-row top-k -> compact lists.
  *   stem_bsa_prefill    causal block-sparse flash attention over those lists
- *                       (bf16, or fp8 e4m3 with per-block scales).
+ *                       (bf16, or fp8 e4m3 with per-block scales, with e4m3 or
+ *                       fp16 attention weights for P.V).
  * plus stem_dense_prefill, the library's own dense causal attention (the
  * baseline every speed-up is measured against), and two variants of stage 3:
  * stem_bsa_prefill_paged (fp8 K/V in a page pool addressed by a block table)
  * and stem_bsa_prefill_q64 (lists over 64-query rows against 128-key blocks).
  *
  * Sources: AngelSlim documentation "Stem: Rethinking Causal Information Flow in
- * Sparse Attention" (features/sparse_attention/stem.md) §2.1-2.3 and the §6
- * parameter table; gist.science summary of the Stem paper, §2.1 (TPD budget)
+ * Sparse Attention" §2.1-2.3 and the §6 parameter table; gist.science summary of the Stem paper, §2.1 (TPD budget)
  * and §2.2 (OAM metric).
  *
  * Conventions shared by every entry point:
