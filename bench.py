@@ -203,7 +203,17 @@ def cpu_baseline(w, q, k, v, idx, cnt, gpu_flop_dense, budget_s=20.0):
             "kind": "oracle",
             "sample": "; ".join(parts) + f"; measured {t_vn + t_sc + t_tk + t_bs:.1f} s, scaled by work "
                       f"to an estimated {est_total:.0f} s per layer (extrapolated)",
-            "est_stage_s": {"score": est_score, "schedule": est_topk, "bsa": est_bsa}}
+            "est_stage_s": {"score": est_score, "schedule": est_topk, "bsa": est_bsa},
+            "host_cpu": host_cpu_model()}
+
+
+def host_cpu_model() -> str:
+    """The host CPU's model name and logical CPU count, from /proc/cpuinfo."""
+    try:
+        names = [ln.split(":", 1)[1].strip() for ln in open("/proc/cpuinfo") if ln.startswith("model name")]
+        return f"{names[0]} ({len(names)} logical CPUs)" if names else "unknown"
+    except OSError:
+        return "unknown"
 
 
 bsa_pairs_total = [0]
