@@ -207,6 +207,30 @@ def cpu_baseline(w, q, k, v, idx, cnt, gpu_flop_dense, budget_s=20.0):
             "host_cpu": host_cpu_model()}
 
 
+def reference_gemm(torch, dev, n=16384, reps=10):
+    """What a plain dense bf16 contraction sustains on this GPU right now: the
+    vendor GEMM behind torch.mm on contiguous N(0,1) operands (random data: the
+    MFMA clock on this part depends on the operand bits), as a practical
+    reference beside the nameplate peak.  Not part of the measured path."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    a = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16).contiguous()
+    b = torch.randn(n, n, device=dev, generator=g).to(torch.bfloat16).contiguous()
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.mm(a, b, out=c)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return {"op": f"torch.mm bf16 {n}x{n}x{n}", "ms": ms, "tflops": 2.0 * n ** 3 / (ms * 1e-3) / 1e12}
+
+
 def host_cpu_model() -> str:
     """The host CPU's model name and logical CPU count, from /proc/cpuinfo."""
     try:
@@ -335,6 +359,10 @@ def run_main(args):
     log(f"[bench] stem {t_stem:.2f} ms (score {timer.mean('score'):.2f}, schedule "
         f"{timer.mean('schedule'):.3f}, bsa {timer.mean('bsa'):.2f}); dense {t_dense:.2f} ms; "
         f"64x128 blocks {qtimer.mean('q64'):.2f} ms vs square rows {qtimer.mean('bsa'):.2f} ms alternating")
+
+    res["reference_bf16_gemm"] = reference_gemm(torch, dev)
+    log(f"[bench] reference bf16 GEMM (torch.mm, 16384^3, N(0,1) operands): "
+        f"{res['reference_bf16_gemm']['tflops']:.0f} TFLOP/s")
 
     if not args.no_sweep:
         res["density_sweep"] = density_sweep(args, torch, stem, S, dev)
