@@ -101,6 +101,10 @@ def _run(w, fp8):
         paged_equal = bool(torch.equal(pout, out)) and bool(torch.equal(plse, lse))
         note(f"[{w.name}] paged ({kp.shape[0]} pages) equals contiguous: {paged_equal}")
         del kpd, vpd, tabd, pout, plse
+        # the same lists with fp16 weights for P.V
+        out16, lse16 = torch.empty_like(out), torch.empty_like(lse)
+        stem.stem_bsa_prefill(p, qa, ka, va, idx, cnt, SCALE, scales=scales, out=out16, lse=lse16, workspace=aws,
+                              fp16_weights=True)
     out64 = lse64 = None
     if not fp8:
         # 64-query rows, each half given its 128-query row's list
@@ -116,6 +120,11 @@ def _run(w, fp8):
                out=_gather_rows(out, rows), dout=_gather_rows(dout, rows),
                lse={(hi, r): lse[h, r * 128:(r + 1) * 128].to(torch.float64).cpu().numpy()
                     for hi, h in enumerate(HS) for r in rows})
+    if fp8:
+        res["out16"] = _gather_rows(out16, rows)
+        res["lse16"] = {(hi, r): lse16[h, r * 128:(r + 1) * 128].to(torch.float64).cpu().numpy()
+                        for hi, h in enumerate(HS) for r in rows}
+        del out16, lse16
     if out64 is not None:
         res["out64"] = _gather_rows(out64, rows)
         res["lse64"] = {(hi, r): lse64[h, r * 128:(r + 1) * 128].to(torch.float64).cpu().numpy()
@@ -190,6 +199,20 @@ def test_q64_rows_on_sampled_rows(big):
                                       len(KS), SCALE, rows=pairs)
     _compare_rows(big, ro, rl, big["out64"], big["lse64"], (BF16_MAX_ABS, BF16_MEAN_REL),
                   f"{w.name} q64 {len(pairs)} rows")
+
+
+def test_fp8_fp16_weights_on_sampled_rows(big):
+    """The fp8 layer with fp16 weights for P.V: the bf16 output bar on the
+    oracle's attention over the dequantised codes."""
+    if "out16" not in big:
+        pytest.skip("bf16 layer: fp16 weights are an fp8 mode")
+    w = big["w"]
+    qs, ks, vs = big["attn_ref_inputs"]
+    pairs = [(hi, r) for hi in range(len(HS)) for r in big["rows"]]
+    ro, rl = O.block_sparse_attention(qs, ks, vs, big["idx"][HS], big["cnt"][HS], w.cu_seqlens, len(HS),
+                                      len(KS), SCALE, rows=pairs)
+    _compare_rows(big, ro, rl, big["out16"], big["lse16"], (BF16_MAX_ABS, BF16_MEAN_REL),
+                  f"{w.name} fp16 weights {len(pairs)} rows")
 
 
 def test_dense_attention_on_sampled_rows(big):
