@@ -1,0 +1,97 @@
+"""The library enqueues its work on the caller's stream and nowhere else:
+the whole path run on a side stream equals the default-stream run bit for
+bit, and the path captured into a HIP graph (every buffer allocated before
+the capture; the path issues kernel launches only, no memsets or copies)
+replays correctly on new inputs, each replay checked against an eager run
+with eager work and synchronisation in between."""
+import math
+
+import torch
+import pytest
+
+import block_sparse_attention_stem_amd as stem
+import stem_synth as S
+from gpu_common import dev, note, to_dev
+
+pytestmark = pytest.mark.gpu
+
+SCALE = 1.0 / math.sqrt(128.0)
+LENS = (512, 1280, 768)
+HQ, HKV = 8, 2
+KSTART, MU, ALPHA = [2, 5, 3], 0.5, 0.7
+
+
+class Buffers:
+    """Every output and workspace of one pass, allocated up front."""
+
+    def __init__(self, p):
+        d = dev()
+        self.kcap = stem.stem_max_kept(p, KSTART, MU, ALPHA, 1, 2)
+        self.scores = torch.empty((p.Hq, p.R, p.max_nb), dtype=torch.float32, device=d)
+        self.sws = torch.empty(stem.stem_score_workspace_bytes(p), dtype=torch.uint8, device=d)
+        self.idx = torch.empty((p.Hq, p.R, self.kcap), dtype=torch.int32, device=d)
+        self.cnt = torch.empty((p.Hq, p.R), dtype=torch.int32, device=d)
+        self.aws = torch.empty(stem.stem_attn_workspace_bytes(p), dtype=torch.uint8, device=d)
+        self.out = torch.empty((p.T, p.Hq, 128), dtype=torch.bfloat16, device=d)
+        self.lse = torch.empty((p.Hq, p.T), dtype=torch.float32, device=d)
+
+
+def _pass(p, q, k, v, b, stream=None):
+    stem.stem_score(p, q, k, v, scores=b.scores, workspace=b.sws, stream=stream)
+    stem.stem_schedule_topk(p, b.scores, KSTART, MU, ALPHA, 1, 2, b.kcap, b.idx, b.cnt, stream=stream)
+    stem.stem_bsa_prefill(p, q, k, v, b.idx, b.cnt, SCALE, out=b.out, lse=b.lse, workspace=b.aws, stream=stream)
+
+
+def _same(a, b):
+    return all(torch.equal(x, y) for x, y in ((a.scores, b.scores), (a.idx, b.idx), (a.cnt, b.cnt),
+                                              (a.out, b.out), (a.lse, b.lse)))
+
+
+def test_side_stream_equals_default_stream():
+    p = stem.Problem(S.cu_from_lengths(LENS), HQ, HKV)
+    q, k, v = to_dev(*S.make_qkv(LENS, HQ, HKV, 128, 21, True))
+    ref, side_b = Buffers(p), Buffers(p)
+    _pass(p, q, k, v, ref)
+    side = torch.cuda.Stream()                     # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _pass(p, q, k, v, side_b)                  # the wrapper passes torch's current stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert _same(ref, side_b)
+    # and an explicit stream argument from the default stream's context
+    exp_b = Buffers(p)
+    side.wait_stream(torch.cuda.current_stream())
+    _pass(p, q, k, v, exp_b, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert _same(ref, exp_b)
+
+
+def test_graph_capture_replays_match_eager():
+    p = stem.Problem(S.cu_from_lengths(LENS), HQ, HKV)
+    q, k, v = to_dev(*S.make_qkv(LENS, HQ, HKV, 128, 31, True))
+    gb = Buffers(p)
+    # warm up on a side stream, as graph capture expects
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _pass(p, q, k, v, gb)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _pass(p, q, k, v, gb)
+    eb = Buffers(p)
+    for rep, seed in enumerate((41, 42, 43)):
+        nq, nk, nv = to_dev(*S.make_qkv(LENS, HQ, HKV, 128, seed, True))
+        q.copy_(nq)
+        k.copy_(nk)
+        v.copy_(nv)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        _pass(p, q, k, v, eb)                      # eager, same inputs
+        torch.cuda.synchronize()
+        note(f"  graph replay {rep} (inputs seed {seed})")
+        assert _same(gb, eb), f"replay {rep} differs from the eager pass"
