@@ -26,7 +26,7 @@
  *    default stream).  The host never waits for the device.  Every call
  *    enqueues kernel launches only (no memset, copy or allocation), so a
  *    sequence of calls can be captured into a HIP graph and replayed; launch
- *    arguments (shapes, k_start, scales of the softmax) are fixed at capture.
+ *    arguments (shapes, k_start, the softmax scale, ...) are fixed at capture.
  *  - Arguments are validated before anything is enqueued; an invalid call
  *    returns a non-zero stem_status_t and enqueues nothing.  A launch failure
  *    returns STEM_ERR_HIP.  Device-side faults surface at the caller's next
