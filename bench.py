@@ -207,6 +207,31 @@ def cpu_baseline(w, q, k, v, idx, cnt, gpu_flop_dense, budget_s=20.0):
             "host_cpu": host_cpu_model()}
 
 
+def graph_pass_ms(torch, fns, reps=20):
+    """Capture the calls in `fns` (every buffer already allocated) into a HIP
+    graph and time its replay: the pass without host launch gaps."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for fn in fns:
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for fn in fns:
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
 def reference_gemm(torch, dev, n=16384, reps=10):
     """What a plain dense bf16 contraction sustains on this GPU right now: the
     vendor GEMM behind torch.mm on contiguous N(0,1) operands (random data: the
@@ -561,12 +586,17 @@ def length_sweep(args, torch, stem, S, dev):
         t_stem = timer.mean("score") + timer.mean("schedule") + timer.mean("bsa")
         t_dense = dt.mean("dense")
         rho = bsa_pairs(idx, cnt, p) / (p.Hq * L * (L + 1) / 2)
+        # short prompts: the same three calls replayed from a HIP graph (no
+        # host launch gaps between the six kernels)
+        t_graph = graph_pass_ms(torch, fns) if L <= 32768 else None
         pts.append({"seq_len": L, "k_start": ks, "computed_pair_fraction": rho,
                     "stem_ms": t_stem, "score_ms": timer.mean("score"), "schedule_ms": timer.mean("schedule"),
                     "bsa_ms": timer.mean("bsa"), "dense_ms": t_dense, "speedup": t_dense / t_stem,
+                    "stem_graph_ms": t_graph,
                     "effective_tflops": dense_flop([L], 32) / (t_stem * 1e-3) / 1e12})
-        log(f"[bench]   N={L}: stem {t_stem:.3f} ms (score {timer.mean('score'):.3f}) dense {t_dense:.3f} ms "
-            f"-> {t_dense / t_stem:.2f}x")
+        log(f"[bench]   N={L}: stem {t_stem:.3f} ms (score {timer.mean('score'):.3f}"
+            + (f"; one graph replay {t_graph:.3f}" if t_graph is not None else "")
+            + f") dense {t_dense:.3f} ms -> {t_dense / t_stem:.2f}x")
         del qd, kd, vd, scores, ws, idx, cnt, out, aws
         torch.cuda.empty_cache()
     return {"workload": "one layer, 32q/8kv, d128, ~25% kept (alpha 0.7, mu 0.5, 1 sink + 2 window)",
