@@ -319,8 +319,9 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
   };
 
   // Step c: wait for chunk c+1, barrier (chunk c's fragments, read in step
-  // c-1, are out of its stage everywhere), load chunk c+4 into that stage,
-  // read chunk c+1's fragments, run chunk c's MFMAs from registers.
+  // c-1, are out of its stage everywhere), then run chunk c's MFMAs from
+  // registers with the loads of chunk c+4 into that stage and the fragment
+  // reads of chunk c+1 issued between them.
   Frags fr[2];
   score_static_for<kStages>([&](auto C_) {
     stage_issue(std::integral_constant<int, decltype(C_)::value>{}, decltype(C_)::value);
@@ -335,13 +336,32 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
       constexpr int later = (kChunks - 2 - c < kStages - 2 ? kChunks - 2 - c : kStages - 2) * 4;
       score_wait_vmcnt<later>();
       score_sync();
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (c + kStages < kChunks)
         stage_issue(std::integral_constant<int, c % kStages>{}, c + kStages);
       stage_read(std::integral_constant<int, (c + 1) % kStages>{}, fr[(c + 1) & 1]);
+      mfmas(fr[c & 1]);
+      // The loads and fragment reads go between the MFMAs (none depends on
+      // them): per group of four MFMAs, one fragment read after each of the
+      // first three and one tile load after the first.  Issued as a burst
+      // before the MFMAs they held both waves of a SIMD off the matrix core
+      // at the start of every step.
+      score_static_for<4>([&](auto) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+      __builtin_amdgcn_sched_barrier(0);
+      mfmas(fr[c & 1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    mfmas(fr[c & 1]);
-    __builtin_amdgcn_sched_barrier(0);
   });
 
   // ---- epilogue: causal mask, 16x16 max-pool, scale, bonus
