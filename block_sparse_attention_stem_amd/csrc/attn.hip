@@ -59,8 +59,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // including the asynchronous K/V loads meant to overlap the next phase.
 // Here each wave waits for its own LDS reads (lgkmcnt(0)); completion of the
 // direct loads is awaited explicitly with wait_vmcnt before the barrier that
-// publishes them.  The empty asm statements keep the compiler from moving
-// memory accesses across the barrier.
+// publishes them.  The signal fences keep the compiler from moving memory
+// accesses across the barrier (register-only work such as MFMAs may still
+// cross it).
 __device__ __forceinline__ void block_sync() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0xC07F);            // lgkmcnt(0), vmcnt/expcnt untouched
@@ -799,16 +800,17 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
 #pragma unroll
   for (int u = 0; u < 4; ++u) o[u] = f32x16{};
 
-  // kNext: what the step prefetches for the next block (kNone nothing, kV8
-  // its V^T image (the fp16 one under kPV16, else the e4m3 one), kV16 the fp16
-  // image of a diagonal block); may_diag: whether this block may be the
-  // diagonal one (only the last listed block can be); v16_pending: its fp16
-  // image was requested last, so the wait at the top leaves it in flight.
-  enum { kNone = 0, kV8 = 1, kV16 = 2 };
-  auto step = [&](int J, int Jn, int kNext, bool may_diag, bool v16_pending) __attribute__((always_inline)) {
-    if (kPV16 || v16_pending) wait_vmcnt<8>(); else wait_vmcnt<4>();
+  // One step per listed block J: K of J is in flight when it starts.  The
+  // first barrier publishes K of J and marks every wave's P.V of the previous
+  // block done, so V of J (the fp16 image for the diagonal block or under
+  // kPV16, else the e4m3 one) is requested there and lands during Q.K^T and
+  // the softmax; the second barrier publishes it and frees the K tile for the
+  // next block's K, which lands during P.V.
+  auto step = [&](int J, int Jn, bool has_next, bool may_diag) __attribute__((always_inline)) {
+    wait_vmcnt<0>();
     block_sync();
     const bool diag = may_diag && (J == w.I);
+    if (kPV16 || diag) issue_v16(J); else issue_v8(J);
     const int sr = zrow + J;
     const float c = cq * a.k_scale[(size_t)sr * a.Hkv + w.g];
     const float vs = a.v_scale[(size_t)sr * a.Hkv + w.g];
@@ -823,7 +825,7 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
     softmax_fp8(s, diag, qloc, lg, c, __builtin_amdgcn_logf(vs), __builtin_amdgcn_rcpf(vs), R, L, o);
     wait_vmcnt<0>();
     block_sync();
-    if (kNext != kNone) issue_k(Jn);
+    if (has_next) issue_k(Jn);
     if (!kPV16 && !diag) {
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
@@ -851,38 +853,17 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
           o[u] = mfma_f16_32x32x16(as_f16x8(ld16(vhad + 32 * kRow16 * u + 16 * cc)), pk, o[u]);
       }
     }
-    block_sync();
-    if (kNext == kV8 && !kPV16) issue_v8(Jn);
-    if (kNext == kV16 || (kNext == kV8 && kPV16)) issue_v16(Jn);
   };
 
-  // Lists are ascending, so only the last block can be the diagonal one: the
-  // loop body handles blocks whose successor is not last; the last two steps
-  // are peeled so every prefetch count is fixed at its call site.
+  // Lists are ascending, so only the last block can be the diagonal one.
   int J = kSparse ? clampJ(list[0]) : 0;
-  const bool first_v16 = (n_blk == 1) && (J == w.I);
   issue_k(J);
-  if (first_v16 || kPV16) issue_v16(J); else issue_v8(J);
-  for (int b = 0; b + 2 < n_blk; ++b) {
+  for (int b = 0; b + 1 < n_blk; ++b) {
     const int Jn = kSparse ? clampJ(list[b + 1]) : b + 1;
-    step(J, Jn, kV8, false, false);
+    step(J, Jn, true, false);
     J = Jn;
   }
-  if (n_blk >= 2) {
-    const int Jl = kSparse ? clampJ(list[n_blk - 1]) : n_blk - 1;
-    if (Jl == w.I) {
-      step(J, Jl, kV16, false, false);
-      J = Jl;
-      step(J, 0, kNone, true, true);
-    } else {
-      step(J, Jl, kV8, false, false);
-      J = Jl;
-      step(J, 0, kNone, false, false);
-    }
-  } else {
-    if (first_v16) step(J, 0, kNone, true, true);
-    else step(J, 0, kNone, false, false);
-  }
+  step(J, 0, false, true);
 
   const float l_tot = L + __shfl_xor(L, 32, 64);
   write_out(orow, o, 1.f / l_tot, lg);
