@@ -88,6 +88,7 @@ int stem_score(const stem_problem_t *p, const void *q, const void *k, const void
   if (stride != 8) return STEM_ERR_UNSUPPORTED;
   if (chunk_size < kBlock || chunk_size % kBlock != 0) return STEM_ERR_INVALID_ARG;
   if (!(norm > 0.f) || !isfinite(norm) || !isfinite(beta) || beta < 0.f) return STEM_ERR_INVALID_ARG;
+  if (s.max_nb > kMaxScoreBlocks) return STEM_ERR_UNSUPPORTED;
   const size_t need = stem_score_workspace_bytes(p);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return STEM_ERR_WORKSPACE;
 

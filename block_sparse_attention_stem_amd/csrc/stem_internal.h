@@ -13,6 +13,7 @@ constexpr int kHeadDim = 128;         // head dimension
 constexpr int kMaxSeqsPerLaunch = 64; // sequences described inline per launch
 constexpr int kMaxRowBlocks = 2048;   // top-k row length limit (256K tokens)
 constexpr int kMaxListBlocks = 4096;  // 64-query-row attention: longest sequence (key blocks)
+constexpr int kMaxScoreBlocks = 65536; // scoring: longest sequence (key blocks; 32-bit tile indexing)
 
 // Packed-batch description passed BY VALUE to every kernel (no device
 // metadata buffers).  Offsets are global: tok[z] is the first packed token of

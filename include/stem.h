@@ -103,6 +103,7 @@ const char *stem_status_string(int status);
  * q, k, v: bf16.  stride must divide block_size (else INVALID_ARG); stride 8
  * is the one implemented (others return UNSUPPORTED).  chunk_size is a
  * positive multiple of block_size (it orders the work, it changes no value).
+ * Sequences of more than 65536 blocks (8M tokens) return UNSUPPORTED.
  * workspace: device memory of at least stem_score_workspace_bytes(p) bytes,
  * 256-byte aligned; its contents on return are unspecified.
  * ------------------------------------------------------------------------- */

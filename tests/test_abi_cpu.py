@@ -98,6 +98,7 @@ def test_score_argument_errors():
     assert _score(stem.Problem([0, 1024], 4, 2, head_dim=64)) == 2
     assert _score(stem.Problem([0, 1024], 4, 2, block_size=64)) == 2
     assert _score(stem.Problem([0, 1024, 1024], 4, 2)) == 1   # empty sequence
+    assert _score(stem.Problem([0, 128 * 65537], 4, 2), wsb=1 << 30) == 2   # longer than 65536 blocks
     assert stem.stem_score_workspace_bytes(stem.Problem([0, 1024], 4, 2)) == 256
 
 
