@@ -11,6 +11,14 @@ functions carry the C names (include/stem.h):
 
 Importing this module never falls back to anything: if libstem.so is missing
 or fails to load, calls raise.
+
+Streams: work goes on `stream` (a torch.cuda.Stream), else on torch's current
+stream.  Tensors a call allocates itself (outputs, workspaces) come from
+torch's caching allocator on the current stream; with another stream, make it
+wait on the current one first (stream.wait_stream) or pass preallocated
+tensors.  Temporaries a call drops before returning (its own workspaces, the
+intermediate scores and lists of stem_prefill) are recorded on `stream`, so
+their memory is not handed out again before the work queued there is done.
 """
 from __future__ import annotations
 
@@ -128,6 +136,12 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on_stream(t: Optional[torch.Tensor], stream):
+    """Record a temporary on `stream` (see the module docstring)."""
+    if stream is not None and t is not None:
+        t.record_stream(stream)
+
+
 def _check(fn: str, st: int):
     if st != STEM_OK:
         raise StemError(fn, st)
@@ -155,11 +169,15 @@ def stem_score(p: Problem, q, k, v, stride: int = 8, chunk_size: int = 2048, nor
         scores = torch.empty((p.Hq, p.R, p.max_nb), dtype=torch.float32, device=q.device)
     _need(scores, "scores", torch.float32, (p.Hq, p.R, p.max_nb))
     nbytes = stem_score_workspace_bytes(p)
-    if workspace is None:
+    own_ws = workspace is None
+    if own_ws:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     st = lib.stem_score(p.ref, _ptr(q), _ptr(k), _ptr(v), stride, chunk_size, float(norm),
-                        float(beta), _ptr(scores), _ptr(workspace), workspace.numel(), _stream(stream))
+                        float(beta), _ptr(scores), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                        _stream(stream))
     _check("stem_score", st)
+    if own_ws:
+        _on_stream(workspace, stream)
     return scores
 
 
@@ -232,10 +250,11 @@ def stem_attn_workspace_bytes(p: Problem, dtype: int = STEM_DTYPE_BF16) -> int:
     return int(load_library().stem_attn_workspace_bytes(p.ref, dtype))
 
 
-def _attn_workspace(p: Problem, dt: int, workspace, device):
+def _attn_workspace(p: Problem, dt: int, workspace, device, stream):
     n = stem_attn_workspace_bytes(p, dt)
     if workspace is None:
         workspace = torch.empty(n, dtype=torch.uint8, device=device)
+        _on_stream(workspace, stream)     # dropped on return, read by work queued on `stream`
     if workspace.numel() * workspace.element_size() < n:
         raise ValueError(f"workspace: need {n} bytes")
     return workspace
@@ -262,7 +281,7 @@ def stem_bsa_prefill(p: Problem, q, k, v, block_idx, block_cnt, softmax_scale: O
         lse = torch.empty((p.Hq, p.T), dtype=torch.float32, device=q.device)
     if lse is not None:
         _need(lse, "lse", torch.float32, (p.Hq, p.T))
-    ws = _attn_workspace(p, dt, workspace, q.device)
+    ws = _attn_workspace(p, dt, workspace, q.device, stream)
     st = lib.stem_bsa_prefill(p.ref, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(qs), _ptr(kss), _ptr(vs),
                               _ptr(block_idx), _ptr(block_cnt), int(block_idx.shape[2]), scale,
                               _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
@@ -292,7 +311,7 @@ def stem_bsa_prefill_q64(p: Problem, q, k, v, block_idx, block_cnt, softmax_scal
         lse = torch.empty((p.Hq, p.T), dtype=torch.float32, device=q.device)
     if lse is not None:
         _need(lse, "lse", torch.float32, (p.Hq, p.T))
-    ws = _attn_workspace(p, dt, workspace, q.device)
+    ws = _attn_workspace(p, dt, workspace, q.device, stream)
     st = lib.stem_bsa_prefill_q64(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(block_idx), _ptr(block_cnt),
                                   int(block_idx.shape[2]), scale, _ptr(out), _ptr(lse), _ptr(ws),
                                   ws.numel() * ws.element_size(), _stream(stream))
@@ -339,7 +358,7 @@ def stem_bsa_prefill_paged(p: Problem, q, k_pages, v_pages, block_table, block_i
         lse = torch.empty((p.Hq, p.T), dtype=torch.float32, device=q.device)
     if lse is not None:
         _need(lse, "lse", torch.float32, (p.Hq, p.T))
-    ws = _attn_workspace(p, STEM_DTYPE_FP8_E4M3, workspace, q.device)
+    ws = _attn_workspace(p, STEM_DTYPE_FP8_E4M3, workspace, q.device, stream)
     st = lib.stem_bsa_prefill_paged(p.ref, _ptr(q8), _ptr(kp), _ptr(vpg), _ptr(qs), _ptr(kss), _ptr(vs),
                                     _ptr(block_table), int(block_table.shape[1]), n_pages, _ptr(block_idx),
                                     _ptr(block_cnt), int(block_idx.shape[2]), scale, _ptr(out), _ptr(lse),
@@ -363,7 +382,7 @@ def stem_dense_prefill(p: Problem, q, k, v, softmax_scale: Optional[float] = Non
         lse = torch.empty((p.Hq, p.T), dtype=torch.float32, device=q.device)
     if lse is not None:
         _need(lse, "lse", torch.float32, (p.Hq, p.T))
-    ws = _attn_workspace(p, dt, workspace, q.device)
+    ws = _attn_workspace(p, dt, workspace, q.device, stream)
     st = lib.stem_dense_prefill(p.ref, dt, _ptr(q), _ptr(k), _ptr(v), _ptr(qs), _ptr(kss), _ptr(vs),
                                 scale, _ptr(out), _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                 _stream(stream))
@@ -385,6 +404,8 @@ def stem_prefill(p: Problem, q, k, v, k_start, mu: float = 0.5, alpha: float = 1
     """
     s = stem_score(p, q, k, v, stride, chunk_size, norm, beta, stream=stream)
     idx, cnt = stem_schedule_topk(p, s, k_start, mu, alpha, n_init, n_window, stream=stream)
+    for t in (s, idx, cnt):
+        _on_stream(t, stream)             # intermediates, dropped on return
     if fp8_inputs is None:
         if fp16_weights:
             raise ValueError("fp16_weights applies to fp8_inputs only")

@@ -95,3 +95,25 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         note(f"  graph replay {rep} (inputs seed {seed})")
         assert _same(gb, eb), f"replay {rep} differs from the eager pass"
+
+
+def test_side_stream_with_the_calls_own_temporaries():
+    """stem_prefill on a side stream allocates its workspaces, scores and lists
+    itself and drops them on return; while its kernels may still run, the
+    current stream allocates and fills fresh memory.  The temporaries are
+    recorded on the side stream, so that memory is not handed out again early
+    and the result equals the default-stream call."""
+    p = stem.Problem(S.cu_from_lengths(LENS), HQ, HKV)
+    q, k, v = to_dev(*S.make_qkv(LENS, HQ, HKV, 128, 51, True))
+    ref = stem.stem_prefill(p, q, k, v, KSTART, MU, ALPHA, 1, 2)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        out = stem.stem_prefill(p, q, k, v, KSTART, MU, ALPHA, 1, 2, stream=side)
+        junk = [torch.full((1 << 18,), float(rep), device=dev()) for _ in range(16)]
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        note(f"  side-stream stem_prefill {rep}: {len(junk)} buffers filled meanwhile")
+        assert torch.equal(out, ref), f"side-stream call {rep} differs"
+        del junk
