@@ -177,9 +177,30 @@ def test_many_sequences_span_several_launches():
     idx, cnt = stem.stem_schedule_topk(p, torch.from_numpy(ref).to(dev()), 2, 0.5, 1.0, 1, 1)
     ri, rc = O.schedule_topk(ref, cu, [2] * len(lens), 0.5, 1.0, 1, 1, idx.shape[2])
     lists_equal(idx.cpu().numpy(), cnt.cpu().numpy(), ri, rc, "72 seqs")
-    out = stem.stem_bsa_prefill(p, qd, kd, vd, idx, cnt, SCALE)
-    ro, _ = O.block_sparse_attention(qf, kf, vf, ri, rc, cu, 2, 1, SCALE)
+    out, lse = stem.stem_bsa_prefill(p, qd, kd, vd, idx, cnt, SCALE, want_lse=True)
+    ro, rl = O.block_sparse_attention(qf, kf, vf, ri, rc, cu, 2, 1, SCALE)
     check_out(f64(out), ro, BF16_MAX_ABS, BF16_MEAN_REL, "72 seqs")
+    check_lse(lse.cpu().numpy().astype(np.float64), rl, "72 seqs")
+    dout = stem.stem_dense_prefill(p, qd, kd, vd, SCALE)
+    do, _ = O.dense_causal_attention(qf, kf, vf, cu, 2, 1, SCALE)
+    check_out(f64(dout), do, BF16_MAX_ABS, BF16_MEAN_REL, "72 seqs dense")
+    i64, c64 = random_q64_lists(lens, 2, seed=11)
+    o64 = stem.stem_bsa_prefill_q64(p, qd, kd, vd, torch.from_numpy(i64).to(dev()), torch.from_numpy(c64).to(dev()),
+                                    SCALE)
+    r64, _ = O.block_sparse_attention(qf, kf, vf, i64, c64, cu, 2, 1, SCALE, q_block=64)
+    check_out(f64(o64), r64, BF16_MAX_ABS, BF16_MEAN_REL, "72 seqs 64x128")
+    # fp8, contiguous and paged: the block table is indexed across launches
+    (q8, k8, v8), (qs, ks, vs) = quantize_fp8(q, k, v, lens)
+    qa, ka, va = to_dev(q8, k8, v8)
+    o8, l8 = stem.stem_bsa_prefill(p, qa, ka, va, idx, cnt, SCALE, scales=to_dev(qs, ks, vs), want_lse=True)
+    ro8, rl8 = O.block_sparse_attention(dequant(q8, qs), dequant(k8, ks), dequant(v8, vs), ri, rc, cu, 2, 1, SCALE)
+    check_out(f64(o8), ro8, FP8_MAX_ABS, None, "72 seqs fp8")
+    check_lse(l8.cpu().numpy().astype(np.float64), rl8, "72 seqs fp8")
+    kp, vp, ksp, vsp, table = page_pool(k8, v8, ks, vs, lens, spare=6, seed=11)
+    kpd, vpd, tabd = to_dev(kp, vp, table)
+    op, lp = stem.stem_bsa_prefill_paged(p, qa, kpd, vpd, tabd, idx, cnt, SCALE, scales=to_dev(qs, ksp, vsp),
+                                         want_lse=True)
+    assert torch.equal(op, o8) and torch.equal(lp, l8), "72 seqs: paged differs from contiguous"
 
 
 def test_topk_tie_stress():
