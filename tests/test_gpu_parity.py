@@ -260,10 +260,11 @@ def test_fp8_full_lists_equal_dense(fp8_small):
 
 # ------------------------------------------------------- head-group shapes ----
 
-@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 1)])
+@pytest.mark.parametrize("Hq,Hkv", [(4, 4), (8, 1), (10, 2), (9, 3)])
 def test_head_group_ratios(Hq, Hkv):
-    """Multi-head (1 query head per KV head) and 8 query heads on one KV head:
-    scores, lists and attention through the whole path."""
+    """Multi-head (1 query head per KV head), 8 query heads on one KV head, and
+    odd group sizes (5 and 3 query heads per KV head, an odd KV head count):
+    scores, lists and attention through the whole path, bf16 and fp8."""
     lens = (640, 1408)
     cu = S.cu_from_lengths(lens)
     q, k, v = make_inputs(lens, Hq, Hkv, seed=11)
@@ -285,6 +286,13 @@ def test_head_group_ratios(Hq, Hkv):
     dout = stem.stem_dense_prefill(p, qd, kd, vd, SCALE)
     do, _ = O.dense_causal_attention(qf, kf, vf, cu, Hq, Hkv, SCALE)
     check_out(f64(dout), do, BF16_MAX_ABS, BF16_MEAN_REL, f"dense Hq={Hq} Hkv={Hkv}")
+    (q8, k8, v8), (qs, kss, vs) = quantize_fp8(q, k, v, lens)
+    o8, l8 = stem.stem_bsa_prefill(p, *to_dev(q8, k8, v8), idx, cnt, SCALE, scales=to_dev(qs, kss, vs),
+                                   want_lse=True)
+    ro8, rl8 = O.block_sparse_attention(dequant(q8, qs), dequant(k8, kss), dequant(v8, vs), ri, rc, cu, Hq, Hkv,
+                                        SCALE)
+    check_out(f64(o8), ro8, FP8_MAX_ABS, None, f"fp8 bsa Hq={Hq} Hkv={Hkv}")
+    check_lse(l8.cpu().numpy().astype(np.float64), rl8, f"fp8 bsa Hq={Hq} Hkv={Hkv}")
 
 
 def test_score_parameters_beta_zero_and_norm():
