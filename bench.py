@@ -403,7 +403,7 @@ def fp8_varlen(args, torch, stem, S, dev):
     """The fp8 varlen batch: sequences of 8K, 16K, 32K and 72K tokens packed
     into 128K, 32 q / 8 kv heads.  Scoring runs on the bf16 tensors, attention
     on their per-(block, head) e4m3 quantisation (done by the harness, outside
-    the timed region).  Layers 0-4 use alpha 1.0 and layers 5-35 alpha 0.7;
+    the timed region); scoring on the e4m3 codes is timed beside it.  Layers 0-4 use alpha 1.0 and layers 5-35 alpha 0.7;
     both kinds are timed on the inputs of layer 0 (the time depends on the
     lists, not on the draw), and the 36-layer total is 5 t(1.0) + 31 t(0.7).
     """
@@ -453,13 +453,17 @@ def fp8_varlen(args, torch, stem, S, dev):
         log(f"[bench]   fp8 {tag}: layer {t_layer:.2f} ms (bsa {timer.mean('bsa'):.2f} ms, "
             f"rho {pairs / dense_pairs:.4f})")
     idx, cnt = lists["alpha_0.7"]
-    dtimer = StageTimer(torch, ["dense", "paged", "e4m3_weights", "fp16_weights"])
+    dtimer = StageTimer(torch, ["dense", "paged", "e4m3_weights", "fp16_weights", "score_bf16", "score_fp8"])
+    scores8 = torch.empty_like(scores)
     dfn = [lambda: stem.stem_dense_prefill(p, qa, ka, va, scales=scl, out=out, workspace=aws),
            lambda: stem.stem_bsa_prefill_paged(p, qa, kpd, vpd, tabd, idx, cnt, scales=pscl, out=out,
                                                workspace=aws),
            lambda: stem.stem_bsa_prefill(p, qa, ka, va, idx, cnt, scales=scl, out=out, workspace=aws),
            lambda: stem.stem_bsa_prefill(p, qa, ka, va, idx, cnt, scales=scl, out=out, workspace=aws,
-                                         fp16_weights=True)]
+                                         fp16_weights=True),
+           lambda: stem.stem_score(p, qd, kd, vd, w_lo.stride, w_lo.chunk_size, w_lo.norm, w_lo.beta, scores, ws),
+           lambda: stem.stem_score(p, qa, ka, va, w_lo.stride, w_lo.chunk_size, w_lo.norm, w_lo.beta, scores8, ws,
+                                   scales=scl)]
     dtimer.run(dfn)
     torch.cuda.synchronize()
     devs = [dtimer.run(dfn) for _ in range(3)]
@@ -483,12 +487,22 @@ def fp8_varlen(args, torch, stem, S, dev):
         L_["skip_overhead"] = L_["stages_ms"]["bsa"] / (L_["computed_pair_fraction"] * t_dense) - 1.0
     total = 5 * layers["alpha_1.0"]["ms"] + 31 * lo["ms"]
     log(f"[bench]   fp8 dense {t_dense:.2f} ms; 36 layers {total:.1f} ms vs dense {36 * t_dense:.1f} ms")
+    # scoring on the e4m3 codes (stem_score_fp8) in place of the bf16 tensors,
+    # timed alternately with the bf16 scoring call; the layer figures swap the
+    # score stage for it (its lists select the same number of blocks)
+    t_s16, t_s8 = dtimer.mean("score_bf16"), dtimer.mean("score_fp8")
+    total8 = total - 36 * (t_s16 - t_s8)
+    fp8_scoring = {"score_ms": t_s8, "bf16_score_ms_alternating": t_s16, "score_speedup": t_s16 / t_s8,
+                   "ms_36_layers": total8, "speedup_vs_dense_36_layers": 36 * t_dense / total8}
+    log(f"[bench]   fp8 scoring: {t_s8:.2f} ms vs {t_s16:.2f} ms on bf16 (alternating); "
+        f"36 layers {total8:.1f} ms ({36 * t_dense / total8:.2f}x dense)")
     return {"workload": "fp8 e4m3 varlen, seqlens 8192/16384/32768/73728 (T=131072), 32q/8kv, "
                         "d128, per-(128-block, head) scales, k_start 18/35/70/156, mu 0.5, 1 sink + 2 window",
             "layers": layers, "dense_ms": t_dense,
             "dense_tflops": flop_dense / (t_dense * 1e-3) / 1e12,
             "ms_36_layers": total, "dense_ms_36_layers": 36 * t_dense,
             "speedup_vs_dense_36_layers": 36 * t_dense / total,
+            "fp8_scoring": fp8_scoring,
             "roofline": {"bound": "mfma", "kernel": "attn_fp8_kernel<sparse>", "achieved": lo["bsa_tflops"],
                          "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                          "frac": lo["bsa_tflops"] / PEAK_FP8_TFLOPS}}

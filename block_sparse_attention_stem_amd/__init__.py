@@ -44,7 +44,7 @@ STATUS = {0: "STEM_OK", 1: "STEM_ERR_INVALID_ARG", 2: "STEM_ERR_UNSUPPORTED",
 DEFAULTS = dict(block_size=128, stride=8, chunk_size=2048, norm=1.0,
                 initial_blocks=4, window_size=4, stem_alpha=1.0, beta=0.2)
 
-EXPORTED = ("stem_status_string", "stem_score_workspace_bytes", "stem_score",
+EXPORTED = ("stem_status_string", "stem_score_workspace_bytes", "stem_score", "stem_score_fp8",
             "stem_schedule_topk", "stem_tpd_budget", "stem_kept_count", "stem_max_kept",
             "stem_attn_workspace_bytes", "stem_bsa_prefill", "stem_dense_prefill",
             "stem_bsa_prefill_paged", "stem_bsa_prefill_q64")
@@ -84,6 +84,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.stem_score_workspace_bytes.restype = sz
     lib.stem_score.argtypes = [P, vp, vp, vp, i32, i32, f32, f32, vp, vp, sz, vp]
     lib.stem_score.restype = ctypes.c_int
+    lib.stem_score_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, i32, f32, f32, vp, vp, sz, vp]
+    lib.stem_score_fp8.restype = ctypes.c_int
     lib.stem_schedule_topk.argtypes = [P, vp, ctypes.POINTER(f64), f64, f64, i32, i32, i32, vp, vp, vp]
     lib.stem_schedule_topk.restype = ctypes.c_int
     lib.stem_tpd_budget.argtypes = [i32, i32, f64, f64, f64]
@@ -159,12 +161,26 @@ def stem_score_workspace_bytes(p: Problem) -> int:
 
 def stem_score(p: Problem, q, k, v, stride: int = 8, chunk_size: int = 2048, norm: float = 1.0,
                beta: float = 0.2, scores: Optional[torch.Tensor] = None,
-               workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Block scores fp32 [Hq][R][max_nb] (-inf for J > I and J >= nb)."""
+               workspace: Optional[torch.Tensor] = None, stream=None, scales=None) -> torch.Tensor:
+    """Block scores fp32 [Hq][R][max_nb] (-inf for J > I and J >= nb).
+
+    bf16 q, k, v; or e4m3 codes with scales = (q_scale, k_scale, v_scale) as in
+    stem_bsa_prefill (stem_score_fp8: the scores of the dequantised values)."""
     lib = load_library()
-    _need(q, "q", torch.bfloat16, (p.T, p.Hq, p.d))
-    _need(k, "k", torch.bfloat16, (p.T, p.Hkv, p.d))
-    _need(v, "v", torch.bfloat16, (p.T, p.Hkv, p.d))
+    fp8 = q.dtype != torch.bfloat16
+    if fp8:
+        q, k, v = (t.view(torch.uint8) if t.dtype == torch.float8_e4m3fn else t for t in (q, k, v))
+        if scales is None or len(scales) != 3:
+            raise ValueError("e4m3 scoring needs (q_scale, k_scale, v_scale)")
+        _need(scales[0], "q_scale", torch.float32, (p.R, p.Hq))
+        _need(scales[1], "k_scale", torch.float32, (p.R, p.Hkv))
+        _need(scales[2], "v_scale", torch.float32, (p.R, p.Hkv))
+    elif scales is not None:
+        raise ValueError("bf16 scoring takes no scales")
+    dt = torch.uint8 if fp8 else torch.bfloat16
+    _need(q, "q", dt, (p.T, p.Hq, p.d))
+    _need(k, "k", dt, (p.T, p.Hkv, p.d))
+    _need(v, "v", dt, (p.T, p.Hkv, p.d))
     if scores is None:
         scores = torch.empty((p.Hq, p.R, p.max_nb), dtype=torch.float32, device=q.device)
     _need(scores, "scores", torch.float32, (p.Hq, p.R, p.max_nb))
@@ -172,10 +188,16 @@ def stem_score(p: Problem, q, k, v, stride: int = 8, chunk_size: int = 2048, nor
     own_ws = workspace is None
     if own_ws:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    st = lib.stem_score(p.ref, _ptr(q), _ptr(k), _ptr(v), stride, chunk_size, float(norm),
-                        float(beta), _ptr(scores), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                        _stream(stream))
-    _check("stem_score", st)
+    wsb = workspace.numel() * workspace.element_size()
+    if fp8:
+        st = lib.stem_score_fp8(p.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(scales[0]), _ptr(scales[1]), _ptr(scales[2]),
+                                stride, chunk_size, float(norm), float(beta), _ptr(scores), _ptr(workspace), wsb,
+                                _stream(stream))
+        _check("stem_score_fp8", st)
+    else:
+        st = lib.stem_score(p.ref, _ptr(q), _ptr(k), _ptr(v), stride, chunk_size, float(norm),
+                            float(beta), _ptr(scores), _ptr(workspace), wsb, _stream(stream))
+        _check("stem_score", st)
     if own_ws:
         _on_stream(workspace, stream)
     return scores
@@ -395,14 +417,21 @@ def stem_prefill(p: Problem, q, k, v, k_start, mu: float = 0.5, alpha: float = 1
                  stride: int = DEFAULTS["stride"], chunk_size: int = DEFAULTS["chunk_size"],
                  norm: float = DEFAULTS["norm"], beta: float = DEFAULTS["beta"],
                  fp8_inputs=None, softmax_scale: Optional[float] = None, stream=None,
-                 fp16_weights: bool = False):
+                 fp16_weights: bool = False, fp8_scoring: bool = False):
     """The whole path for one layer: score -> schedule/top-k -> block-sparse attention.
 
     Scoring runs on the bf16 q, k, v.  With `fp8_inputs = (q8, k8, v8, (qs, ks, vs))`
     the attention stage runs on those e4m3 tensors instead (with fp16_weights,
-    P.V keeps fp16 weights; see stem_bsa_prefill).
+    P.V keeps fp16 weights; see stem_bsa_prefill), and with fp8_scoring the
+    scoring stage too (stem_score_fp8; q, k, v may then be None).
     """
-    s = stem_score(p, q, k, v, stride, chunk_size, norm, beta, stream=stream)
+    if fp8_scoring:
+        if fp8_inputs is None:
+            raise ValueError("fp8_scoring needs fp8_inputs")
+        q8, k8, v8, sc = fp8_inputs
+        s = stem_score(p, q8, k8, v8, stride, chunk_size, norm, beta, stream=stream, scales=sc)
+    else:
+        s = stem_score(p, q, k, v, stride, chunk_size, norm, beta, stream=stream)
     idx, cnt = stem_schedule_topk(p, s, k_start, mu, alpha, n_init, n_window, stream=stream)
     for t in (s, idx, cnt):
         _on_stream(t, stream)             # intermediates, dropped on return

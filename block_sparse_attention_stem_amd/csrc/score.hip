@@ -13,6 +13,7 @@
 //           the 16x16 max-pool, the 1/(sqrt(d) s n) scale and the bonus fused
 //           into the epilogue.  Only the causal triangle of 256x256 strided
 //           tiles is launched; scores never touch HBM before pooling.
+#include <type_traits>
 #include <utility>
 
 #include "stem_internal.h"
@@ -54,9 +55,48 @@ __global__ __launch_bounds__(256) void vnorm_kernel(const __bf16 *__restrict__ v
   }
 }
 
+// e4m3 V: ||V_t||^2 = vs_J^2 sum_d code_d^2 with vs_J the block's V scale.
+// 8 lanes per token row (8 x 16 codes), 32 rows per pass.
+__global__ __launch_bounds__(256) void vnorm_fp8_kernel(const uint8_t *__restrict__ v, const float *__restrict__ vsc,
+                                                        float *__restrict__ ell, int Hkv, int R) {
+  const int kb = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x, sub = tid & 7, rowg = tid >> 3;
+  __shared__ float red[32];
+  float emax = 0.f;
+  for (int t = rowg; t < kBlock; t += 32) {
+    const size_t tok = (size_t)kb * kBlock + t;
+    const u32x4 raw = ld16(v + (tok * Hkv + g) * kHeadDim + sub * 16);
+    float e = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], true);
+      e = fmaf(lo[0], lo[0], e);
+      e = fmaf(lo[1], lo[1], e);
+      e = fmaf(hi[0], hi[0], e);
+      e = fmaf(hi[1], hi[1], e);
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) e += __shfl_xor(e, o, 64);
+    emax = fmaxf(emax, e);
+  }
+  if (sub == 0) red[rowg] = emax;
+  __syncthreads();
+  if (tid == 0) {
+    float m = red[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) m = fmaxf(m, red[i]);
+    const float vs = vsc[(size_t)kb * Hkv + g];
+    ell[(size_t)g * R + kb] = logf(fmaxf(vs * vs * m, 1e-30f));
+  }
+}
+
 hipError_t launch_vnorm(const ScoreLaunch &a, hipStream_t s) {
   dim3 grid(a.R, a.Hkv);
-  hipLaunchKernelGGL(vnorm_kernel, grid, dim3(256), 0, s, (const __bf16 *)a.v, a.ell, a.Hkv, a.R);
+  if (a.fp8)
+    hipLaunchKernelGGL(vnorm_fp8_kernel, grid, dim3(256), 0, s, (const uint8_t *)a.v, a.v_scale, a.ell, a.Hkv, a.R);
+  else
+    hipLaunchKernelGGL(vnorm_kernel, grid, dim3(256), 0, s, (const __bf16 *)a.v, a.ell, a.Hkv, a.R);
   return hipGetLastError();
 }
 
@@ -121,6 +161,12 @@ hipError_t launch_vstats(const ScoreLaunch &a, const SeqTable &t, hipStream_t s)
 // % 4, so the fragment reads of an MFMA hit every bank once.  The
 // permutation is applied on the global side of the loads (each lane fetches
 // the piece that belongs at its fixed LDS slot).
+//
+// e4m3 inputs (kFp8): the same tile, rows and loads; a chunk is 64 codes
+// (one 64-byte piece of one token row, 16 chunks), one 32x32x64 fp8 MFMA step
+// whose 32-byte lane operand is two 16-byte pieces.  Q and K scales are
+// constant over a block pair's 16 x 16 strided cells, so they multiply the
+// pooled maximum.
 constexpr int kTileS = 256;                 // strided rows per tile side
 constexpr int kScoreBK = 32;                // K elements per chunk
 constexpr int kChunks = 8 * kHeadDim / kScoreBK;   // 32
@@ -129,6 +175,7 @@ constexpr uint32_t kScoreBufWord3 = 0x00020000u;   // raw buffer descriptor word
 
 struct ScoreArgs {
   const __bf16 *q, *k;
+  const float *q_scale, *k_scale;   // kFp8: [R][Hq], [R][Hkv]
   const float *bonus;
   float *scores;
   int32_t Hq, Hkv, R, max_nb, G;
@@ -205,7 +252,10 @@ __device__ __forceinline__ void key_max_rows_and_halves(int (&k)[N]) {
   }
 }
 
+template <bool kFp8>
 __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, int n_items) {
+  constexpr int kEsz = kFp8 ? 1 : 2;                      // bytes per element
+  constexpr int kNChunks = kFp8 ? kChunks / 2 : kChunks;  // 64 codes or 32 bf16 per chunk
   __shared__ __attribute__((aligned(1024))) uint16_t A0[kTileS * kScoreBK];
   __shared__ __attribute__((aligned(1024))) uint16_t A1[kTileS * kScoreBK];
   __shared__ __attribute__((aligned(1024))) uint16_t A2[kTileS * kScoreBK];
@@ -240,7 +290,7 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
   // its last row.
   uint32_t voffA[2], voffB[2];
   {
-    const uint32_t strideA = (uint32_t)a.Hq * kHeadDim * 2 * 8, strideB = (uint32_t)a.Hkv * kHeadDim * 2 * 8;
+    const uint32_t strideA = (uint32_t)a.Hq * kHeadDim * kEsz * 8, strideB = (uint32_t)a.Hkv * kHeadDim * kEsz * 8;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int sl = 64 * (wave + 8 * m) + lane, row = sl >> 2, lc = (sl & 3) ^ ((row >> 2) & 3);
@@ -251,13 +301,16 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
     }
   }
   const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.q + ((tok0 + 8 * (size_t)ibase) * a.Hq + h) * kHeadDim), (short)0, 0x7fffffff, kScoreBufWord3);
+      (void *)((const char *)a.q + ((tok0 + 8 * (size_t)ibase) * a.Hq + h) * kHeadDim * kEsz), (short)0, 0x7fffffff,
+      kScoreBufWord3);
   const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)(a.k + ((tok0 + 8 * (size_t)jbase) * a.Hkv + g) * kHeadDim), (short)0, 0x7fffffff, kScoreBufWord3);
-  const uint32_t tokA = (uint32_t)a.Hq * kHeadDim * 2, tokB = (uint32_t)a.Hkv * kHeadDim * 2;
-  // chunk c: token t = c / 4 of the stride group (reversed for K), dims 32 (c % 4)
+      (void *)((const char *)a.k + ((tok0 + 8 * (size_t)jbase) * a.Hkv + g) * kHeadDim * kEsz), (short)0, 0x7fffffff,
+      kScoreBufWord3);
+  const uint32_t tokA = (uint32_t)a.Hq * kHeadDim * kEsz, tokB = (uint32_t)a.Hkv * kHeadDim * kEsz;
+  // chunk c: token t = c / 4 of the stride group (reversed for K), dims 32 (c % 4);
+  // kFp8: token t = c / 2, codes 64 (c % 2)
   auto issue = [&](int c, uint16_t *Ad, uint16_t *Bd) __attribute__((always_inline)) {
-    const int tt = c >> 2, d2 = (c & 3) * kScoreBK * 2;
+    const int tt = kFp8 ? c >> 1 : c >> 2, d2 = (kFp8 ? (c & 1) : (c & 3)) * 64;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void_t *)(Ad + (wave + 8 * m) * 512), 16, voffA[m],
@@ -278,30 +331,52 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
   // fragment rows wm*64 + 32 mi + frow (A) and wn*128 + 32 nj + frow (B):
   // the permutation key (row / 4) % 4 is (frow / 4) % 4 for all of them
   const int swz = (frow >> 2) & 3;
+  // 16-byte piece read for index x: bf16, k-step x; e4m3, half x of the lane's 32 bytes
   int poff[2];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) poff[ks] = 8 * ((2 * ks + lg) ^ swz);
+  for (int x = 0; x < 2; ++x) poff[x] = 8 * ((kFp8 ? 2 * lg + x : 2 * x + lg) ^ swz);
   const int rowA = (wm * 64 + frow) * kScoreBK, rowB = (wn * 128 + frow) * kScoreBK;
 
-  // Fragments of a chunk: 2 k-steps x (2 A + 4 B) 16-byte reads.
-  typedef u32x4 Frags[2][6];
+  // Fragments of a chunk: 2 k-steps x (2 A + 4 B) 16-byte reads (bf16), or
+  // 2 A + 4 B operands of 32 bytes, each two 16-byte reads (e4m3).
+  typedef u32x4 Frags16[2][6];
+  typedef i32x8 Frags8[6];
+  using Frags = std::conditional_t<kFp8, Frags8, Frags16>;
   auto read_frags = [&](Frags &f, const uint16_t *As, const uint16_t *Bs) __attribute__((always_inline)) {
+    if constexpr (kFp8) {
+      auto ld32 = [&](const uint16_t *row) __attribute__((always_inline)) {
+        const u32x4 lo = ld16(row + poff[0]), hi = ld16(row + poff[1]);
+        return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      };
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+      for (int mi = 0; mi < 2; ++mi) f[mi] = ld32(As + rowA + 32 * mi * kScoreBK);
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi) f[ks][mi] = ld16(As + rowA + 32 * mi * kScoreBK + poff[ks]);
+      for (int nj = 0; nj < 4; ++nj) f[2 + nj] = ld32(Bs + rowB + 32 * nj * kScoreBK);
+    } else {
 #pragma unroll
-      for (int nj = 0; nj < 4; ++nj) f[ks][2 + nj] = ld16(Bs + rowB + 32 * nj * kScoreBK + poff[ks]);
+      for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi) f[ks][mi] = ld16(As + rowA + 32 * mi * kScoreBK + poff[ks]);
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj) f[ks][2 + nj] = ld16(Bs + rowB + 32 * nj * kScoreBK + poff[ks]);
+      }
     }
   };
   auto mfmas = [&](const Frags &f) __attribute__((always_inline)) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    if constexpr (kFp8) {
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int nj = 0; nj < 4; ++nj)
-          acc[mi][nj] = mfma_bf16_32x32x16(as_bf16x8(f[ks][mi]), as_bf16x8(f[ks][2 + nj]), acc[mi][nj]);
+        for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = mfma_fp8_32x32x64(f[mi], f[2 + nj], acc[mi][nj]);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+          for (int nj = 0; nj < 4; ++nj)
+            acc[mi][nj] = mfma_bf16_32x32x16(as_bf16x8(f[ks][mi]), as_bf16x8(f[ks][2 + nj]), acc[mi][nj]);
+    }
   };
   auto stage_issue = [&](auto S_, int c) __attribute__((always_inline)) {
     constexpr int st = decltype(S_)::value;
@@ -329,15 +404,15 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
   score_wait_vmcnt<4 * (kStages - 1)>();
   score_sync();
   stage_read(std::integral_constant<int, 0>{}, fr[0]);
-  score_static_for<kChunks>([&](auto C_) {
+  score_static_for<kNChunks>([&](auto C_) {
     constexpr int c = decltype(C_)::value;
-    if constexpr (c + 1 < kChunks) {
+    if constexpr (c + 1 < kNChunks) {
       // loads of chunks c+2 .. c+3 (4 per wave each) may still fly
-      constexpr int later = (kChunks - 2 - c < kStages - 2 ? kChunks - 2 - c : kStages - 2) * 4;
+      constexpr int later = (kNChunks - 2 - c < kStages - 2 ? kNChunks - 2 - c : kStages - 2) * 4;
       score_wait_vmcnt<later>();
       score_sync();
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (c + kStages < kChunks)
+      if constexpr (c + kStages < kNChunks)
         stage_issue(std::integral_constant<int, c % kStages>{}, c + kStages);
       stage_read(std::integral_constant<int, (c + 1) % kStages>{}, fr[(c + 1) & 1]);
       mfmas(fr[c & 1]);
@@ -346,16 +421,27 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
       // first three and one tile load after the first.  Issued as a burst
       // before the MFMAs they held both waves of a SIMD off the matrix core
       // at the start of every step.
-      score_static_for<4>([&](auto) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      });
+      if constexpr (kFp8) {
+        // 8 MFMAs, 12 fragment reads, 4 loads: per pair of MFMAs, three reads and a load
+        score_static_for<4>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        });
+      } else {
+        score_static_for<4>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        });
+      }
       __builtin_amdgcn_sched_barrier(0);
     } else {
       __builtin_amdgcn_sched_barrier(0);
@@ -407,8 +493,17 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
         const int J = jb / 16 + (lane >> 4);
         const int I0 = ib / 16;
         if (J < nb) {
-          if (I0 < nb) a.scores[srow0 + (size_t)I0 * a.max_nb + J] = m0 * a.scale + bon[J];
-          if (I0 + 1 < nb) a.scores[srow0 + (size_t)(I0 + 1) * a.max_nb + J] = m1 * a.scale + bon[J];
+          if constexpr (kFp8) {
+            // scores of the dequantised values: raw max x q scale of row I x k scale of J
+            const size_t r0 = (size_t)t.row[z];
+            const float sk = a.scale * a.k_scale[(r0 + J) * a.Hkv + g];
+            if (I0 < nb) a.scores[srow0 + (size_t)I0 * a.max_nb + J] = m0 * (sk * a.q_scale[(r0 + I0) * a.Hq + h]) + bon[J];
+            if (I0 + 1 < nb)
+              a.scores[srow0 + (size_t)(I0 + 1) * a.max_nb + J] = m1 * (sk * a.q_scale[(r0 + I0 + 1) * a.Hq + h]) + bon[J];
+          } else {
+            if (I0 < nb) a.scores[srow0 + (size_t)I0 * a.max_nb + J] = m0 * a.scale + bon[J];
+            if (I0 + 1 < nb) a.scores[srow0 + (size_t)(I0 + 1) * a.max_nb + J] = m1 * a.scale + bon[J];
+          }
         }
       }
     }
@@ -430,6 +525,8 @@ hipError_t launch_score(const ScoreLaunch &l, const SeqTable &t, int n_items, hi
   ScoreArgs a;
   a.q = (const __bf16 *)l.q;
   a.k = (const __bf16 *)l.k;
+  a.q_scale = l.q_scale;
+  a.k_scale = l.k_scale;
   a.bonus = l.ell;
   a.scores = l.scores;
   a.Hq = l.Hq;
@@ -438,7 +535,8 @@ hipError_t launch_score(const ScoreLaunch &l, const SeqTable &t, int n_items, hi
   a.max_nb = l.max_nb;
   a.G = l.Hq / l.Hkv;
   a.scale = l.scale;
-  hipLaunchKernelGGL(score_kernel, dim3(n_items), dim3(512), 0, s, a, t, n_items);
+  if (l.fp8) hipLaunchKernelGGL(score_kernel<true>, dim3(n_items), dim3(512), 0, s, a, t, n_items);
+  else hipLaunchKernelGGL(score_kernel<false>, dim3(n_items), dim3(512), 0, s, a, t, n_items);
   return hipGetLastError();
 }
 

@@ -77,13 +77,17 @@ size_t stem_score_workspace_bytes(const stem_problem_t *p) {
   return ((size_t)s.Hkv * s.R * sizeof(float) + 255) / 256 * 256;
 }
 
-int stem_score(const stem_problem_t *p, const void *q, const void *k, const void *v,
-               int32_t stride, int32_t chunk_size, float norm, float beta, float *scores,
-               void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+static int score_common(const stem_problem_t *p, const void *q, const void *k, const void *v,
+                        const float *q_scale, const float *k_scale, const float *v_scale, bool fp8,
+                        int32_t stride, int32_t chunk_size, float norm, float beta, float *scores,
+                        void *workspace, size_t workspace_bytes, void *stream) {
   Shape s;
   int st = check_problem(p, &s);
   if (st != STEM_OK) return st;
   if (!q || !k || !v || !scores) return STEM_ERR_INVALID_ARG;
+  if (fp8 && (!q_scale || !k_scale || !v_scale)) return STEM_ERR_INVALID_ARG;
   if (stride < 1 || kBlock % stride != 0) return STEM_ERR_INVALID_ARG;
   if (stride != 8) return STEM_ERR_UNSUPPORTED;
   if (chunk_size < kBlock || chunk_size % kBlock != 0) return STEM_ERR_INVALID_ARG;
@@ -96,6 +100,10 @@ int stem_score(const stem_problem_t *p, const void *q, const void *k, const void
   a.q = q;
   a.k = k;
   a.v = v;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.fp8 = fp8;
   a.scores = scores;
   a.ell = (float *)workspace;
   a.Hq = s.Hq;
@@ -136,6 +144,24 @@ int stem_score(const stem_problem_t *p, const void *q, const void *k, const void
     if (launch_score(a, t, (int)items, hs) != hipSuccess) return STEM_ERR_HIP;
   }
   return STEM_OK;
+}
+
+
+extern "C" {
+
+int stem_score(const stem_problem_t *p, const void *q, const void *k, const void *v,
+               int32_t stride, int32_t chunk_size, float norm, float beta, float *scores,
+               void *workspace, size_t workspace_bytes, void *stream) {
+  return score_common(p, q, k, v, nullptr, nullptr, nullptr, false, stride, chunk_size, norm, beta, scores,
+                      workspace, workspace_bytes, stream);
+}
+
+int stem_score_fp8(const stem_problem_t *p, const void *q, const void *k, const void *v,
+                   const float *q_scale, const float *k_scale, const float *v_scale, int32_t stride,
+                   int32_t chunk_size, float norm, float beta, float *scores, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+  return score_common(p, q, k, v, q_scale, k_scale, v_scale, true, stride, chunk_size, norm, beta, scores,
+                      workspace, workspace_bytes, stream);
 }
 
 int32_t stem_tpd_budget(int32_t I, int32_t nb, double k_start, double mu, double alpha) {

@@ -107,10 +107,12 @@ __host__ __device__ inline int score_pairs(int nb) {
 // ---------------------------------------------------------------- launchers
 struct ScoreLaunch {
   const void *q, *k, *v;
+  const float *q_scale, *k_scale, *v_scale;   // e4m3 inputs: per (block, head); else null
   float *scores, *ell;          // ell: workspace [Hkv][R] (log norms, then bonus)
   int32_t Hq, Hkv, R, max_nb;
   int32_t stride, chunk_size;
   float scale, beta;
+  bool fp8;
 };
 hipError_t launch_vnorm(const ScoreLaunch &a, hipStream_t s);
 hipError_t launch_vstats(const ScoreLaunch &a, const SeqTable &t, hipStream_t s);

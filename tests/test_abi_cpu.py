@@ -100,6 +100,17 @@ def test_score_argument_errors():
     assert _score(stem.Problem([0, 1024, 1024], 4, 2)) == 1   # empty sequence
     assert _score(stem.Problem([0, 128 * 65537], 4, 2), wsb=1 << 30) == 2   # longer than 65536 blocks
     assert stem.stem_score_workspace_bytes(stem.Problem([0, 1024], 4, 2)) == 256
+    # e4m3 scoring: every scale pointer is required; the rest as stem_score
+    lib = stem.load_library()
+    p = stem.Problem([0, 1024], 4, 2)
+
+    def s8(qs=FAKE, ks=FAKE, vs=FAKE, stride=8, ws=FAKE):
+        return lib.stem_score_fp8(p.ref, FAKE, FAKE, FAKE, qs, ks, vs, stride, 2048, 1.0, 0.2, FAKE, ws, 1 << 20, None)
+    assert s8(qs=None) == 1
+    assert s8(ks=None) == 1
+    assert s8(vs=None) == 1
+    assert s8(stride=4) == 2
+    assert s8(ws=None) == 4
 
 
 def test_schedule_argument_errors():

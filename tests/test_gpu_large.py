@@ -101,6 +101,11 @@ def _run(w, fp8):
         paged_equal = bool(torch.equal(pout, out)) and bool(torch.equal(plse, lse))
         note(f"[{w.name}] paged ({kp.shape[0]} pages) equals contiguous: {paged_equal}")
         del kpd, vpd, tabd, pout, plse
+        # scoring on the e4m3 codes (stem_score_fp8), with its own lists
+        scores8 = torch.empty_like(scores)
+        stem.stem_score(p, qa, ka, va, w.stride, w.chunk_size, w.norm, w.beta, scores8, ws, scales=scales)
+        fp8_scores = scores8.cpu().numpy()
+        del scores8
         # the same lists with fp16 weights for P.V
         out16, lse16 = torch.empty_like(out), torch.empty_like(lse)
         stem.stem_bsa_prefill(p, qa, ka, va, idx, cnt, SCALE, scales=scales, out=out16, lse=lse16, workspace=aws,
@@ -121,6 +126,7 @@ def _run(w, fp8):
                lse={(hi, r): lse[h, r * 128:(r + 1) * 128].to(torch.float64).cpu().numpy()
                     for hi, h in enumerate(HS) for r in rows})
     if fp8:
+        res["fp8_scores"] = fp8_scores
         res["out16"] = _gather_rows(out16, rows)
         res["lse16"] = {(hi, r): lse16[h, r * 128:(r + 1) * 128].to(torch.float64).cpu().numpy()
                         for hi, h in enumerate(HS) for r in rows}
@@ -154,6 +160,24 @@ def test_scores_on_sampled_rows(big):
                          rows=rows)
     gpu = big["scores"][HS][:, rows]
     check_scores(gpu, ref[:, rows], f"{w.name} {len(HS)} heads x {len(rows)} rows")
+
+
+def test_fp8_scores_on_sampled_rows_and_their_lists(big):
+    """Scoring on the e4m3 codes: the oracle's scores of the dequantised values
+    on sampled rows, and every list selected from those scores bit-exact."""
+    if "fp8_scores" not in big:
+        pytest.skip("bf16 layer: e4m3 scoring applies to the fp8 layer")
+    w, rows = big["w"], big["rows"]
+    qs, ks, vs = big["attn_ref_inputs"]
+    bonus = O.value_bonus(vs, w.cu_seqlens, 128, w.beta)
+    ref = O.block_scores(qs, ks, bonus, w.cu_seqlens, len(HS), len(KS), 128, w.stride, 128, w.norm, rows=rows)
+    check_scores(big["fp8_scores"][HS][:, rows], ref[:, rows], f"{w.name} e4m3 scoring {len(HS)} heads x {len(rows)} rows")
+    ri, rc = O.schedule_topk(big["fp8_scores"], w.cu_seqlens, w.k_start, w.mu, w.alpha, w.n_init, w.n_window,
+                             big["kcap"])
+    idx, cnt = stem.stem_schedule_topk(stem.Problem(w.cu_seqlens, w.num_q_heads, w.num_kv_heads),
+                                       torch.from_numpy(big["fp8_scores"]).to(dev()), w.k_start, w.mu, w.alpha,
+                                       w.n_init, w.n_window, big["kcap"])
+    lists_equal(idx.cpu().numpy(), cnt.cpu().numpy(), ri, rc, f"{w.name} e4m3 scoring")
 
 
 def test_every_list_bit_exact(big):

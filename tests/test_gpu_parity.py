@@ -246,6 +246,32 @@ def test_fp8_bsa_and_dense(fp8_small):
     check_out(f64(dout), do, FP8_MAX_ABS, None, "fp8 dense")
 
 
+def test_fp8_scores_and_lists(fp8_small):
+    """stem_score_fp8 on the e4m3 codes: the oracle's scores of the dequantised
+    values (value bonus included) to the score bar, and the lists selected
+    from them bit-exact; also with beta = 0 and norm = 2."""
+    lens, _, (q8, k8, v8), (qs, ks, vs), (qf, kf, vf) = fp8_small
+    cu = S.cu_from_lengths(lens)
+    p = stem.Problem(cu, 4, 2)
+    qa, ka, va = to_dev(q8, k8, v8)
+    sc = to_dev(qs, ks, vs)
+    for beta, norm in ((0.2, 1.0), (0.0, 2.0)):
+        s = stem.stem_score(p, qa, ka, va, 8, 2048, norm, beta, scales=sc)
+        ref = O.block_scores(qf, kf, O.value_bonus(vf, cu, 128, beta), cu, 4, 2, 128, 8, 2048, norm)
+        check_scores(s.cpu().numpy(), ref, f"fp8 scores beta {beta} norm {norm}")
+    idx, cnt = stem.stem_schedule_topk(p, s, [1, 3, 4], 0.5, 1.0, 1, 1)
+    ri, rc = O.schedule_topk(s.cpu().numpy(), cu, [1, 3, 4], 0.5, 1.0, 1, 1, idx.shape[2])
+    lists_equal(idx.cpu().numpy(), cnt.cpu().numpy(), ri, rc, "fp8 scores")
+    # the whole fp8 layer through stem_prefill with fp8 scoring equals the three calls
+    s1 = stem.stem_score(p, qa, ka, va, scales=sc)
+    i1, c1 = stem.stem_schedule_topk(p, s1, [1, 3, 4], 0.5, 1.0, 2, 2)
+    o1 = stem.stem_bsa_prefill(p, qa, ka, va, i1, c1, scales=sc)
+    o2 = stem.stem_prefill(p, None, None, None, [1, 3, 4], 0.5, 1.0, n_init=2, n_window=2,
+                           fp8_inputs=(qa, ka, va, sc), fp8_scoring=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
 def test_fp8_full_lists_equal_dense(fp8_small):
     lens, _, (q8, k8, v8), (qs, ks, vs), _ = fp8_small
     cu = S.cu_from_lengths(lens)

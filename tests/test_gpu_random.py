@@ -1,5 +1,6 @@
 """GPU parity on seeded random problem shapes: the whole path (scores, lists,
-bf16 / fp8 / fp8 with fp16 weights / paged / 64x128 attention) against the oracle, over random
+bf16 / fp8 / fp8 with fp16 weights / paged / 64x128 attention, scoring on
+e4m3 codes) against the oracle, over random
 sequence counts and lengths, head ratios and schedule parameters.  Each
 case is deterministic (its seed fixes every draw) and small enough for the
 oracle to check every output."""
@@ -83,3 +84,12 @@ def test_random_shapes_whole_path(seed):
     assert torch.equal(op, o8) and torch.equal(lp, l8), f"random {seed}: paged differs from contiguous"
     o16 = stem.stem_bsa_prefill(p, qa, ka, va, idx, cnt, scale, scales=scl, fp16_weights=True)
     check_out(f64(o16), ro8, BF16_MAX_ABS, BF16_MEAN_REL, f"random {seed} fp8 inputs, fp16 weights")
+
+    # scoring on the e4m3 codes, and the lists selected from those scores
+    qq, kq, vq = dequant(q8, qs), dequant(k8, ks), dequant(v8, vs)
+    s8 = stem.stem_score(p, qa, ka, va, 8, 2048, 1.0, beta, scales=scl)
+    ref8 = O.block_scores(qq, kq, O.value_bonus(vq, cu, 128, beta), cu, Hq, Hkv, 128, 8, 2048, 1.0)
+    check_scores(s8.cpu().numpy(), ref8, f"random {seed} e4m3 scoring")
+    i8, c8 = stem.stem_schedule_topk(p, s8, k_start, mu, alpha, n_init, n_window, kcap)
+    ri8, rc8 = O.schedule_topk(s8.cpu().numpy(), cu, k_start, mu, alpha, n_init, n_window, kcap)
+    lists_equal(i8.cpu().numpy(), c8.cpu().numpy(), ri8, rc8, f"random {seed} e4m3 scoring")
