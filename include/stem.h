@@ -4,7 +4,8 @@
  * The path has three stages, each one entry point:
  *   stem_score          block-level scoring: stride-s anti-diagonal down-sampled
  *                       Q.K^T, max-pooled to block x block scores, plus the
- *                       output-aware value bonus.
+ *                       output-aware value bonus (stem_score_fp8: the same on
+ *                       e4m3 codes with per-block scales).
  *   stem_schedule_topk  Token-Position-Decay budget per query block, sink and
  *                       window blocks forced, per-row top-k -> compact lists.
  *   stem_bsa_prefill    causal block-sparse flash attention over those lists
