@@ -120,8 +120,9 @@ int stem_score(const stem_problem_t *p, const void *q, const void *k, const void
  * maximum is multiplied by its query and key block scales, which are constant
  * over the pair's strided cells, and the value bonus uses
  * ||V_t||^2 = v_scale^2 sum_d code_d^2.  The fp8 MFMA sums its 64 products
- * per step to about 2^-15 of their absolute sum (not fp32 rounding), a few
- * 1e-4 of a score on unit-variance inputs.  A null scale pointer returns
+ * per step to about 2^-15 of their absolute sum (not fp32 rounding): on
+ * unit-variance inputs the scores stay within 3e-5 of max(|score|, 1) of the
+ * exact scores of the dequantised values.  A null scale pointer returns
  * INVALID_ARG; everything else as stem_score (same workspace size). */
 int stem_score_fp8(const stem_problem_t *p, const void *q, const void *k, const void *v,
                    const float *q_scale, const float *k_scale, const float *v_scale,
