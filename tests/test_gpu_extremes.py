@@ -23,7 +23,8 @@ import block_sparse_attention_stem_amd as stem
 import oracle as O
 import stem_synth as S
 from gpu_common import (BF16_MAX_ABS, BF16_MEAN_REL, FP8_MAX_ABS, bf16_half_ulp, check_lse, check_out,
-                        dequant, dev, f64, note, quantize_fp8, random_q64_lists, to_dev)
+                        check_scores, dequant, dev, f64, lists_equal, note, quantize_fp8, random_q64_lists,
+                        to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -189,3 +190,32 @@ def test_fp8_fp16_weights_meet_the_bf16_bar_on_peaked_logits(gain):
     full = stem.stem_bsa_prefill(p, *to_dev(q8, k8, v8), torch.from_numpy(fi).to(dev()),
                                  torch.from_numpy(fc).to(dev()), SCALE, scales=sc, fp16_weights=True)
     assert torch.equal(full, dout), "every block listed must equal the dense call"
+
+
+def test_scores_with_all_zero_blocks():
+    """An all-zero V block has ||V||^2 = 0: its log norm is the floor ln(1e-30),
+    which drags the z-score of every other block of its sequence up; an
+    all-zero K block scores 0 (plus its bonus) against every query, and an
+    all-zero Q block scores 0 against every key.  bf16 scoring and scoring on
+    e4m3 codes (a zero block quantises with scale 1 to zero codes) against the
+    oracle, and the lists selected from them."""
+    cu = S.cu_from_lengths(LENS)
+    p = stem.Problem(cu, HQ, HKV)
+    q, k, v = S.make_qkv(LENS, HQ, HKV, 128, 17, True)
+    v[256 + 128:256 + 256, 1] = 0          # second block of the second sequence, KV head 1
+    k[256 + 768 + 384:256 + 768 + 512, 0] = 0
+    q[256 + 768 + 640:256 + 768 + 768] = 0
+    ks_, mu, alpha = [1, 3, 4], 0.5, 1.0
+    ref = O.block_scores(f64(q), f64(k), O.value_bonus(f64(v), cu, 128, 0.2), cu, HQ, HKV, 128, 8, 2048, 1.0)
+    s = stem.stem_score(p, *to_dev(q, k, v))
+    check_scores(s.cpu().numpy(), ref, "zero blocks, bf16 scoring")
+    (q8, k8, v8), (qs, kss, vs) = quantize_fp8(q, k, v, LENS)
+    assert float(vs[3, 1]) == 1.0 and int(v8[256 + 128:256 + 256, 1].sum()) == 0
+    ref8 = O.block_scores(dequant(q8, qs), dequant(k8, kss), O.value_bonus(dequant(v8, vs), cu, 128, 0.2), cu,
+                          HQ, HKV, 128, 8, 2048, 1.0)
+    s8 = stem.stem_score(p, *to_dev(q8, k8, v8), scales=to_dev(qs, kss, vs))
+    check_scores(s8.cpu().numpy(), ref8, "zero blocks, e4m3 scoring")
+    for tag, sc in (("bf16", s), ("e4m3", s8)):
+        idx, cnt = stem.stem_schedule_topk(p, sc, ks_, mu, alpha, 1, 1)
+        ri, rc = O.schedule_topk(sc.cpu().numpy(), cu, ks_, mu, alpha, 1, 1, idx.shape[2])
+        lists_equal(idx.cpu().numpy(), cnt.cpu().numpy(), ri, rc, f"zero blocks, {tag} scoring")
