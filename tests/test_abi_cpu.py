@@ -198,6 +198,19 @@ def test_q64_attention_argument_errors():
     assert call(stem.Problem([0, 128 * 4097], 4, 2).ref, f, f, f, f, f, 8, 0.1, f, None, f, W, None) == 2
 
 
+def test_binding_rejects_mismatched_scoring_arguments():
+    """The binding's e4m3-scoring checks fire before any device call."""
+    p = stem.Problem([0, 1024], 4, 2)
+    codes = [torch.zeros(1024, h, 128, dtype=torch.uint8) for h in (4, 2, 2)]
+    with pytest.raises(ValueError, match="e4m3 scoring needs"):
+        stem.stem_score(p, *codes)
+    bf = [torch.zeros(1024, h, 128, dtype=torch.bfloat16) for h in (4, 2, 2)]
+    with pytest.raises(ValueError, match="takes no scales"):
+        stem.stem_score(p, *bf, scales=(torch.ones(8, 4), torch.ones(8, 2), torch.ones(8, 2)))
+    with pytest.raises(ValueError, match="fp8_scoring needs fp8_inputs"):
+        stem.stem_prefill(p, *bf, [4], fp8_scoring=True)
+
+
 def test_package_defaults_match_the_doc_table():
     import json
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "stem_doc_defaults.json")))
