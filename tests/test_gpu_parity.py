@@ -162,6 +162,13 @@ def test_chunk_size_changes_no_score(varlen):
     outs = [stem.stem_score(p, qd, kd, vd, 8, c).cpu() for c in (128, 1024, 2048, 4096)]
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
+    # and on the e4m3 codes
+    (q8, k8, v8), scl = quantize_fp8(q, k, v, lens)
+    qa, ka, va = to_dev(q8, k8, v8)
+    sc = to_dev(*scl)
+    outs8 = [stem.stem_score(p, qa, ka, va, 8, c, scales=sc).cpu() for c in (128, 1024, 2048, 4096)]
+    for o in outs8[1:]:
+        assert torch.equal(o, outs8[0])
 
 
 def test_many_sequences_span_several_launches():
@@ -319,6 +326,13 @@ def test_head_group_ratios(Hq, Hkv):
                                         SCALE)
     check_out(f64(o8), ro8, FP8_MAX_ABS, None, f"fp8 bsa Hq={Hq} Hkv={Hkv}")
     check_lse(l8.cpu().numpy().astype(np.float64), rl8, f"fp8 bsa Hq={Hq} Hkv={Hkv}")
+    # scoring on the e4m3 codes and its lists, same head layout
+    qq, kq, vq = dequant(q8, qs), dequant(k8, kss), dequant(v8, vs)
+    s8 = stem.stem_score(p, *to_dev(q8, k8, v8), scales=to_dev(qs, kss, vs))
+    check_scores(s8.cpu().numpy(), _oracle_scores(qq, kq, vq, cu, Hq, Hkv), f"e4m3 scoring Hq={Hq} Hkv={Hkv}")
+    i8, c8 = stem.stem_schedule_topk(p, s8, ks, 0.5, 0.7, 1, 2)
+    ri8, rc8 = O.schedule_topk(s8.cpu().numpy(), cu, ks, 0.5, 0.7, 1, 2, i8.shape[2])
+    lists_equal(i8.cpu().numpy(), c8.cpu().numpy(), ri8, rc8, f"e4m3 scoring Hq={Hq} Hkv={Hkv}")
 
 
 def test_score_parameters_beta_zero_and_norm():
