@@ -117,3 +117,57 @@ def test_side_stream_with_the_calls_own_temporaries():
         note(f"  side-stream stem_prefill {rep}: {len(junk)} buffers filled meanwhile")
         assert torch.equal(out, ref), f"side-stream call {rep} differs"
         del junk
+
+
+def test_graph_capture_of_the_fp8_layer_with_e4m3_scoring():
+    """Scoring on e4m3 codes, selection and fp8 attention captured into one HIP
+    graph; three replays on new codes and scales equal eager runs."""
+    from gpu_common import quantize_fp8
+    p = stem.Problem(S.cu_from_lengths(LENS), HQ, HKV)
+
+    def codes(seed):
+        q, k, v = S.make_qkv(LENS, HQ, HKV, 128, seed, True)
+        (q8, k8, v8), (qs, ks, vs) = quantize_fp8(q, k, v, LENS)
+        return to_dev(q8, k8, v8, qs, ks, vs)
+
+    x = codes(61)
+    kcap = stem.stem_max_kept(p, KSTART, MU, ALPHA, 1, 2)
+    d = dev()
+
+    def bufs():
+        return dict(s=torch.empty((p.Hq, p.R, p.max_nb), dtype=torch.float32, device=d),
+                    sws=torch.empty(stem.stem_score_workspace_bytes(p), dtype=torch.uint8, device=d),
+                    idx=torch.empty((p.Hq, p.R, kcap), dtype=torch.int32, device=d),
+                    cnt=torch.empty((p.Hq, p.R), dtype=torch.int32, device=d),
+                    aws=torch.empty(stem.stem_attn_workspace_bytes(p, stem.STEM_DTYPE_FP8_E4M3), dtype=torch.uint8,
+                                    device=d),
+                    out=torch.empty((p.T, p.Hq, 128), dtype=torch.bfloat16, device=d))
+
+    def run(b):
+        q8, k8, v8, qs, ks, vs = x
+        stem.stem_score(p, q8, k8, v8, scores=b["s"], workspace=b["sws"], scales=(qs, ks, vs))
+        stem.stem_schedule_topk(p, b["s"], KSTART, MU, ALPHA, 1, 2, kcap, b["idx"], b["cnt"])
+        stem.stem_bsa_prefill(p, q8, k8, v8, b["idx"], b["cnt"], SCALE, scales=(qs, ks, vs), out=b["out"],
+                              workspace=b["aws"])
+
+    gb, eb = bufs(), bufs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(gb)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(gb)
+    for rep, seed in enumerate((62, 63, 64)):
+        for dst, src in zip(x, codes(seed)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        run(eb)
+        torch.cuda.synchronize()
+        note(f"  fp8 graph replay {rep} (codes seed {seed})")
+        for key in ("s", "idx", "cnt", "out"):
+            assert torch.equal(gb[key], eb[key]), f"replay {rep}: {key} differs from the eager pass"
