@@ -219,3 +219,39 @@ def test_package_defaults_match_the_doc_table():
     assert stem.DEFAULTS["beta"] == g["beta"]["value"]
     a = g["alpha_list_example"]
     assert list(S.FP8_ALPHAS) == [a["warmup_alpha"]] * a["warmup_layers"] + [a["later_alpha"]] * a["later_layers"]
+
+
+def test_header_is_plain_c_and_links_from_c(tmp_path):
+    """include/stem.h compiles as C99 (-pedantic), and a C program linked
+    against libstem.so calls the host-only entry points (status strings, the
+    budget rule, argument validation) without a GPU."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "abi.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include <string.h>
+#include "stem.h"
+int main(void) {
+  int32_t cu[2] = {0, 4096};
+  stem_problem_t p = {1, cu, 4, 2, 128, 128};
+  double ks = 10.0;
+  if (strcmp(stem_status_string(STEM_ERR_CAPACITY), "STEM_ERR_CAPACITY") != 0) return 1;
+  if (stem_tpd_budget(0, 8, 10.0, 0.5, 1.0) != 10) return 2;
+  if (stem_max_kept(&p, &ks, 0.5, 1.0, 1, 1) != 8) return 3;
+  if (stem_score_workspace_bytes(&p) != 256) return 4;
+  /* a null q is rejected before anything touches a device */
+  if (stem_score(&p, NULL, NULL, NULL, 8, 2048, 1.0f, 0.2f, NULL, NULL, 0, NULL) != STEM_ERR_INVALID_ARG) return 5;
+  printf("ok\n");
+  return 0;
+}
+''')
+    lib_dir = os.path.dirname(stem.LIB_PATH)
+    exe = tmp_path / "abi"
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe), "-L", lib_dir, "-lstem", "-Wl,-rpath," + lib_dir], check=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
