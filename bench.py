@@ -492,8 +492,13 @@ def fp8_varlen(args, torch, stem, S, dev):
     # score stage for it (its lists select the same number of blocks)
     t_s16, t_s8 = dtimer.mean("score_bf16"), dtimer.mean("score_fp8")
     total8 = total - 36 * (t_s16 - t_s8)
+    # algorithmic work: 2*16*16*1024 FLOP per (query head, causal block pair)
+    s_flop = 2.0 * 16 * 16 * 1024 * p.Hq * sum(nb * (nb + 1) / 2 for nb in p.nbs)
+    s_tflops = s_flop / (t_s8 * 1e-3) / 1e12
     fp8_scoring = {"score_ms": t_s8, "bf16_score_ms_alternating": t_s16, "score_speedup": t_s16 / t_s8,
-                   "ms_36_layers": total8, "speedup_vs_dense_36_layers": 36 * t_dense / total8}
+                   "ms_36_layers": total8, "speedup_vs_dense_36_layers": 36 * t_dense / total8,
+                   "roofline": {"bound": "mfma", "kernel": "score_kernel<e4m3>", "achieved": s_tflops,
+                                "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": s_tflops / PEAK_FP8_TFLOPS}}
     log(f"[bench]   fp8 scoring: {t_s8:.2f} ms vs {t_s16:.2f} ms on bf16 (alternating); "
         f"36 layers {total8:.1f} ms ({36 * t_dense / total8:.2f}x dense)")
     return {"workload": "fp8 e4m3 varlen, seqlens 8192/16384/32768/73728 (T=131072), 32q/8kv, "
