@@ -204,8 +204,12 @@ def stem_score(p: Problem, q, k, v, stride: int = 8, chunk_size: int = 2048, nor
 
 
 def _kstart_arr(p: Problem, k_start):
-    ks = [float(k_start)] * (len(p.cu) - 1) if isinstance(k_start, (int, float)) else [float(x) for x in k_start]
-    return (ctypes.c_double * len(ks))(*ks)
+    """One k_start per sequence (a scalar applies to every sequence)."""
+    n = len(p.cu) - 1
+    ks = [float(k_start)] * n if isinstance(k_start, (int, float)) else [float(x) for x in k_start]
+    if len(ks) != n:
+        raise ValueError(f"k_start: expected {n} values (one per sequence), got {len(ks)}")
+    return (ctypes.c_double * n)(*ks)
 
 
 def stem_max_kept(p: Problem, k_start, mu: float, alpha: float, n_init: int, n_window: int) -> int:

@@ -263,11 +263,19 @@ __device__ __forceinline__ void write_empty(__bf16 *orow, float *lse, int lg) {
 // (O and L are then rescaled), so P' <= 2^(kFp8Off + kFp8Lazy) = 430 < 448
 // (the e4m3 maximum) while the largest weight seen so far keeps
 // P' >= 2^(kFp8Off - kFp8Lazy) = 152: small weights stay in e4m3's normal
-// range as far down as with P' = 256 p.  O is rarely touched.  Leaves P' in s.
+// range as far down as with P' = 256 p.  O is rarely touched.  Leaves P' in s
+// and returns cm, the query's largest logit in the block times c.
+//
+// A block is heavy for a query when its largest weight is more than kHeavy
+// of the query's weight sum so far, this block included (heavy_block).
+// An e4m3 weight carries a relative error of up to 2^-4; spread over many
+// keys of similar weight these errors average out, but when a few keys hold
+// a query's attention they do not, and the fp8 kernel then adds a second
+// e4m3 pass with the rounding residual of the weights (see pack_lo_fp8x4).
 constexpr float kFp8Lazy = 0.75f;
 constexpr float kFp8Off = 8.f;
-__device__ __forceinline__ void softmax_fp8(f32x16 (&s)[4], bool diag, int qloc, int lg, float c, float lv,
-                                            float inv_vs, float &R, float &L, f32x16 (&o)[4]) {
+__device__ __forceinline__ float softmax_fp8(f32x16 (&s)[4], bool diag, int qloc, int lg, float c, float lv,
+                                             float inv_vs, float &R, float &L, f32x16 (&o)[4]) {
   if (diag) {
     const int lim = qloc - 4 * lg;          // key > qloc  <=>  (key - 4 lg) > lim
 #pragma unroll
@@ -282,8 +290,11 @@ __device__ __forceinline__ void softmax_fp8(f32x16 (&s)[4], bool diag, int qloc,
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[tt][i]);
   // every query sees at least one key of the block (all of an earlier block,
-  // itself in the diagonal one), so mz is finite
-  const float mz = fmaf(wave_max_xor32(mx), c, lv);
+  // itself in the diagonal one), so cm and mz are finite.  (The two halves of
+  // the query meet through an LDS lane shuffle: v_permlane32_swap needs two
+  // more VALU copies, and this kernel is bound by its VALU issue.)
+  const float cm = wave_max_xor32(mx) * c;
+  const float mz = cm + lv;
   if (__any(mz > R + kFp8Lazy)) {
     const float Rn = fmaxf(R, mz);
     const float f = __builtin_amdgcn_exp2f(R - Rn);   // 0 on the first block (R = -inf), else <= 1
@@ -305,6 +316,16 @@ __device__ __forceinline__ void softmax_fp8(f32x16 (&s)[4], bool diag, int qloc,
       psum += p;
     }
   L = fmaf(psum, inv_vs, L);
+  return cm;
+}
+
+// Whether the block is heavy for this query (see softmax_fp8): its largest
+// weight 2^(cm - R + kFp8Off) (L units) is more than kHeavy of the weight sum
+// of both halves of the query so far.
+constexpr float kHeavy = 0.125f;
+__device__ __forceinline__ bool heavy_block(float cm, float R, float L) {
+  const float l_tot = L + __shfl_xor(L, 32, 64);
+  return __builtin_amdgcn_exp2f(cm - R + kFp8Off) > kHeavy * l_tot;
 }
 
 // ===================================================================== bf16
@@ -703,6 +724,24 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float 
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
+// The residual weights of a heavy block, x - e4m3(x): exact in fp32 and at
+// most 2^-4 |x| (<= 27 for x <= 430), packed to e4m3 again for a second P.V
+// pass; hi + lo leaves a relative error of about 2^-8 per weight.  Residuals
+// of weights below 4 fall into e4m3's subnormal range (steps of 2^-9): an
+// absolute error below 2^-10, negligible next to the block's largest weight
+// (at least 152 whenever it holds the running maximum).
+__device__ __forceinline__ uint32_t pack_lo_fp8x4(float a, float b, float c, float d) {
+  const uint32_t h = pack_fp8x4(a, b, c, d);
+  const auto ab = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, false);
+  const auto cd = __builtin_amdgcn_cvt_pk_f32_fp8((int)h, true);
+  return pack_fp8x4(a - ab[0], b - ab[1], c - cd[0], d - cd[1]);
+}
+
+// e4m3 x e4m3 with an E8M0 block scale on the B operand (127 = 2^0).
+__device__ __forceinline__ f32x16 mfma_fp8_32x32x64_bs(i32x8 a, i32x8 b, f32x16 c, int bscale) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, bscale);
+}
+
 
 template <bool kSparse, bool kPV16>
 __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable t, int rows) {
@@ -806,14 +845,34 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
   // kPV16, else the e4m3 one) is requested there and lands during Q.K^T and
   // the softmax; the second barrier publishes it and frees the K tile for the
   // next block's K, which lands during P.V.
-  auto step = [&](int J, int Jn, bool has_next, bool may_diag) __attribute__((always_inline)) {
+  //
+  // A wave for which the block is heavy (see softmax_fp8) runs a second
+  // e4m3 P.V pass with the rounding residual of its weights (pack_lo_fp8x4,
+  // same V tile): its weights then carry about 2^-8 relative error instead
+  // of 2^-4.  On spread-out attention this is the
+  // first few blocks of a row at most; on concentrated attention it is the
+  // blocks that hold the row's weight.  The decision is per wave (its 32
+  // queries) and needs no exchange.
+  //
+  // The k and v scales of a block are read one step ahead by scalar loads
+  // issued between that step's Q.K^T and its softmax, which waits on no LDS
+  // operation: their latency hides under the exponentials.  (Plain loads in
+  // the step itself made the first wait on them also wait for its V tile.)
+  typedef const __attribute__((address_space(4))) float cfloat;
+  cfloat *ksc_c = (cfloat *)a.k_scale + (size_t)zrow * a.Hkv + w.g;
+  cfloat *vsc_c = (cfloat *)a.v_scale + (size_t)zrow * a.Hkv + w.g;
+  float ksc, vsc;                    // scales of the current block
+  // kDiag: the diagonal block (causal mask, fp16 weights; always a row's
+  // last block).  Otherwise has_next says whether a next block Jn follows.
+  auto step = [&](auto kDiag, int J, int Jn, bool has_next) __attribute__((always_inline)) {
+    constexpr bool diag = decltype(kDiag)::value;
     wait_vmcnt<0>();
     block_sync();
-    const bool diag = may_diag && (J == w.I);
     if (kPV16 || diag) issue_v16(J); else issue_v8(J);
-    const int sr = zrow + J;
-    const float c = cq * a.k_scale[(size_t)sr * a.Hkv + w.g];
-    const float vs = a.v_scale[(size_t)sr * a.Hkv + w.g];
+    const float c = cq * ksc;
+    // a zero V scale (an all-zero block) is taken as 2^-64: its weights still
+    // count in L, and its codes contribute nothing measurable
+    const float vs = fmaxf(vsc, 0x1p-64f);
     f32x16 s[4];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
@@ -822,24 +881,52 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
       for (int ks = 0; ks < 2; ++ks)
         s[tt] = mfma_fp8_32x32x64(ld32(k8ad + 32 * kRow8 * tt + 64 * ks), qf[ks], s[tt]);
     }
-    softmax_fp8(s, diag, qloc, lg, c, __builtin_amdgcn_logf(vs), __builtin_amdgcn_rcpf(vs), R, L, o);
+    if (has_next) {
+      ksc = ksc_c[(size_t)Jn * a.Hkv];
+      vsc = vsc_c[(size_t)Jn * a.Hkv];
+    }
+    const float cm = softmax_fp8(s, diag, qloc, lg, c, __builtin_amdgcn_logf(vs), __builtin_amdgcn_rcpf(vs), R, L, o);
     wait_vmcnt<0>();
     block_sync();
     if (has_next) issue_k(Jn);
     if (!kPV16 && !diag) {
+      // the heavy test runs here, behind the barrier, beside the packing
+      const bool heavy = __any(heavy_block(cm, R, L));
+      // P' packed to e4m3 (and, heavy, its residual) before any MFMA, so the
+      // fp32 weights die here; the residual pass repeats the MFMA stream on
+      // the same V tile
+      i32x8 pkh[2], pkl[2];
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        i32x8 pk;
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int aa = 0; aa < 2; ++aa)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const f32x16 &st = s[2 * cc + aa];
-            pk[4 * aa + j] = (int)pack_fp8x4(st[4 * j + 0], st[4 * j + 1], st[4 * j + 2], st[4 * j + 3]);
+            pkh[cc][4 * aa + j] = (int)pack_fp8x4(st[4 * j + 0], st[4 * j + 1], st[4 * j + 2], st[4 * j + 3]);
           }
+      if (heavy) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const f32x16 &st = s[2 * cc + aa];
+              pkl[cc][4 * aa + j] = (int)pack_lo_fp8x4(st[4 * j + 0], st[4 * j + 1], st[4 * j + 2], st[4 * j + 3]);
+            }
+      }
+#pragma unroll
+      for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
-          o[u] = mfma_fp8_32x32x64(ld32(v8ad + 32 * kRow8 * u + 64 * cc), pk, o[u]);
+          o[u] = mfma_fp8_32x32x64_bs(ld32(v8ad + 32 * kRow8 * u + 64 * cc), pkh[cc], o[u], 127);
+      if (heavy) {      // the residual pass
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            o[u] = mfma_fp8_32x32x64_bs(ld32(v8ad + 32 * kRow8 * u + 64 * cc), pkl[cc], o[u], 127);
       }
     } else {
 #pragma unroll
@@ -855,15 +942,24 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
     }
   };
 
-  // Lists are ascending, so only the last block can be the diagonal one.
+  // Lists are ascending, so only the last block can be the diagonal one:
+  // the loop runs every other block (a last block that is not diagonal
+  // included, with no next K to request), the diagonal block runs last.
   int J = kSparse ? clampJ(list[0]) : 0;
   issue_k(J);
-  for (int b = 0; b + 1 < n_blk; ++b) {
-    const int Jn = kSparse ? clampJ(list[b + 1]) : b + 1;
-    step(J, Jn, true, false);
+  ksc = ksc_c[(size_t)J * a.Hkv];
+  vsc = vsc_c[(size_t)J * a.Hkv];
+  const int last = kSparse ? clampJ(list[n_blk - 1]) : w.I;
+  const int n_loop = last == w.I ? n_blk - 1 : n_blk;
+  using NotDiag = std::integral_constant<bool, false>;
+  using Diag = std::integral_constant<bool, true>;
+  for (int b = 0; b < n_loop; ++b) {
+    const bool has_next = b + 1 < n_blk;
+    const int Jn = has_next ? (kSparse ? clampJ(list[b + 1]) : b + 1) : 0;
+    step(NotDiag{}, J, Jn, has_next);
     J = Jn;
   }
-  step(J, 0, false, true);
+  if (n_loop < n_blk) step(Diag{}, J, 0, false);
 
   const float l_tot = L + __shfl_xor(L, 32, 64);
   write_out(orow, o, 1.f / l_tot, lg);

@@ -7,11 +7,16 @@
 //
 // One wave per (head, query-block row).  Lane l holds candidates J = l + 64 m
 // (m < 32, so rows up to 2048 blocks), i.e. ascending J runs over (m, lane).
-// Scores become order-preserving unsigned keys (NaN -> the key of -inf); the
-// need-th largest key T is found MSB-first with wave-wide counts, then every
-// key > T is taken and keys == T are taken in ascending J until the budget is
-// met: exactly "score descending, lower block index first".  The list is
-// emitted ascending with ballot/mbcnt prefix counts (no sorting network).
+// Scores become order-preserving unsigned keys (NaN -> the key of -inf, -0 ->
+// the key of +0; forced and non-causal slots get key 0, below every real
+// key).  The need-th largest key T is found MSB-first: a candidate threshold
+// is counted with one vector compare per m whose result lands in a 64-bit
+// scalar mask (ballot) and a scalar popcount, so no lane reduction is needed;
+// the bits above the highest bit in which the row's smallest and largest keys
+// differ are common to every key and are taken as given.  Then every key > T
+// is taken and keys == T in ascending J until the budget is met: exactly
+// "score descending, lower block index first".  The list is emitted ascending
+// with ballot/mbcnt prefix counts (no sorting network).
 #include "stem_internal.h"
 #include "gfx950_util.h"
 
@@ -21,19 +26,112 @@ constexpr int kPer = kMaxRowBlocks / 64;   // candidates per lane
 
 __device__ __forceinline__ uint32_t order_key(float s) {
   if (s != s) s = -INFINITY;                       // NaN ranks as -inf
+  s += 0.0f;                                       // -0 -> +0 (equal scores, equal keys)
   const uint32_t u = __float_as_uint(s);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
 }
 
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Wave-wide max / min of an unsigned value (butterfly over the 64 lanes).
+__device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_xor((int)x, o, 64);
+    x = x > y ? x : y;
+  }
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_umin(uint32_t x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = (uint32_t)__shfl_xor((int)x, o, 64);
+    x = x < y ? x : y;
+  }
+  return x;
+}
+
+// One row with candidates in MC slots per lane (J = lane + 64 m, m < MC;
+// slots past the row hold key 0).  MC is a compile-time bound, so no loop
+// over the slots carries a per-slot guard: a guard is a scalar compare and
+// branch, and with one scalar unit per CU they were most of the kernel's
+// time.
+template <int MC>
+__device__ __forceinline__ void topk_row(const float *__restrict__ srow, int32_t *__restrict__ orow,
+                                         int32_t *__restrict__ ocnt, int k_cap, int I, int sink_end, int win0,
+                                         int need, int n_cand, int lane) {
+  uint32_t key[MC];
+  uint32_t forced = 0;                             // bit m: forced block
+  uint32_t kmax = 0u, kmin = 0xffffffffu;
+#pragma unroll
+  for (int m = 0; m < MC; ++m) {
+    key[m] = 0;
+    const int J = lane + 64 * m;
+    if (J <= I) {
+      if ((J < sink_end) || (J >= win0)) forced |= 1u << m;
+      else {
+        key[m] = order_key(srow[J]);
+        kmax = key[m] > kmax ? key[m] : kmax;
+        kmin = key[m] < kmin ? key[m] : kmin;
+      }
+    }
+  }
+
+  uint32_t sel = 0;                                // bit m: selected candidate
+  if (need >= n_cand) {
+#pragma unroll
+    for (int m = 0; m < MC; ++m)
+      if (key[m] != 0u) sel |= 1u << m;
+  } else if (need > 0) {
+    // Every candidate key lies in [lo, hi], so all of them (and T) share the
+    // bits of lo above the highest bit in which lo and hi differ.
+    const uint32_t hi = wave_umax(kmax), lo = wave_umin(kmin);
+    uint32_t T = lo;
+    if (hi != lo) {
+      const int top = 31 - __builtin_clz(hi ^ lo);
+      T = top == 31 ? 0u : (lo & ~((2u << top) - 1u));
+      for (int bit = top; bit >= 0; --bit) {
+        const uint32_t cand = T | (1u << bit);
+        int c = 0;
+#pragma unroll
+        for (int m = 0; m < MC; ++m) c += __popcll(__ballot(key[m] >= cand));
+        if (c >= need) T = cand;
+      }
+    }
+    // T is the need-th largest key, T >= 1: key 0 (no candidate) never counts
+    int c_gt = 0;
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      const uint64_t gm = __ballot(key[m] > T);
+      if ((gm >> lane) & 1u) sel |= 1u << m;
+      c_gt += __popcll(gm);
+    }
+    const int take_eq = need - c_gt;
+    int taken = 0;
+#pragma unroll
+    for (int m = 0; m < MC; ++m) {
+      if (taken < take_eq) {
+        const uint64_t em = __ballot(key[m] == T);
+        if (((em >> lane) & 1u) && taken + lanes_below(em) < take_eq) sel |= 1u << m;
+        taken += __popcll(em);
+      }
+    }
+  }
+
+  int base = 0;
+#pragma unroll
+  for (int m = 0; m < MC; ++m) {
+    const bool in = ((forced | sel) >> m) & 1u;
+    const uint64_t im = __ballot(in);
+    const int pos = base + lanes_below(im);
+    if (in && pos < k_cap) orow[pos] = lane + 64 * m;
+    base += __popcll(im);
+  }
+  for (int p = base + lane; p < k_cap; p += 64) orow[p] = -1;
+  if (lane == 0) *ocnt = base;
 }
 
 __global__ __launch_bounds__(256) void topk_kernel(TopkLaunch a, SeqTable t, int rows) {
@@ -55,74 +153,21 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkLaunch a, SeqTable t, int
   const int n_forced = forced_count(I, a.n_init, a.n_window);
   const int need = kept - n_forced;
   const int n_cand = I + 1 - n_forced;
-  const int mcount = (I + 64) >> 6;                // lanes hold J < 64 * mcount
 
   const float *srow = a.scores + ((size_t)h * a.R + r) * a.max_nb;
-  uint32_t key[kPer];
-  uint32_t valid = 0, forced = 0;                  // bit m: candidate / forced
-#pragma unroll
-  for (int m = 0; m < kPer; ++m) {
-    key[m] = 0;
-    if (m < mcount) {
-      const int J = lane + 64 * m;
-      if (J <= I) {
-        const bool f = (J < sink_end) || (J >= win0);
-        if (f) forced |= 1u << m;
-        else {
-          valid |= 1u << m;
-          key[m] = order_key(srow[J]);
-        }
-      }
-    }
-  }
-
-  uint32_t sel = 0;
-  if (need >= n_cand) {
-    sel = valid;
-  } else if (need > 0) {
-    uint32_t T = 0;
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = T | (1u << bit);
-      int c = 0;
-#pragma unroll
-      for (int m = 0; m < kPer; ++m)
-        if (m < mcount) c += ((valid >> m) & 1u) && key[m] >= cand;
-      if (wave_sum(c) >= need) T = cand;
-    }
-    int c_gt = 0;
-#pragma unroll
-    for (int m = 0; m < kPer; ++m)
-      if (m < mcount && ((valid >> m) & 1u) && key[m] > T) {
-        sel |= 1u << m;
-        ++c_gt;
-      }
-    const int take_eq = need - wave_sum(c_gt);
-    int taken = 0;
-#pragma unroll
-    for (int m = 0; m < kPer; ++m) {
-      if (m < mcount) {
-        const bool eq = ((valid >> m) & 1u) && key[m] == T;
-        const uint64_t em = __ballot(eq);
-        if (eq && taken + lanes_below(em) < take_eq) sel |= 1u << m;
-        taken += __popcll(em);
-      }
-    }
-  }
-
   int32_t *orow = a.idx + ((size_t)h * a.R + r) * a.k_cap;
-  int base = 0;
-#pragma unroll
-  for (int m = 0; m < kPer; ++m) {
-    if (m < mcount) {
-      const bool in = ((forced | sel) >> m) & 1u;
-      const uint64_t im = __ballot(in);
-      const int pos = base + lanes_below(im);
-      if (in && pos < a.k_cap) orow[pos] = lane + 64 * m;
-      base += __popcll(im);
-    }
+  int32_t *ocnt = a.cnt + (size_t)h * a.R + r;
+  // slots per lane: J <= I needs m <= I / 64; rounded up to a multiple of 4
+  switch ((I >> 8) + 1) {
+    case 1: topk_row<4>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
+    case 2: topk_row<8>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
+    case 3: topk_row<12>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
+    case 4: topk_row<16>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
+    case 5: topk_row<20>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
+    case 6: topk_row<24>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
+    case 7: topk_row<28>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
+    default: topk_row<kPer>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
   }
-  for (int p = base + lane; p < a.k_cap; p += 64) orow[p] = -1;
-  if (lane == 0) a.cnt[(size_t)h * a.R + r] = base;
 }
 
 hipError_t launch_topk(const TopkLaunch &a, const SeqTable &t, int rows, hipStream_t s) {

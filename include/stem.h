@@ -187,17 +187,30 @@ size_t stem_attn_workspace_bytes(const stem_problem_t *p, int32_t dtype);   /* F
  * dtype BF16: q, k, v bf16; scales must be NULL.
  * dtype FP8_E4M3: q, k, v are e4m3fn codes (uint8); the real value of an
  *   element of token block b (global) and head x is code * scale[b][x]:
- *   q_scale fp32 [R][Hq], k_scale and v_scale fp32 [R][Hkv].
+ *   q_scale fp32 [R][Hq], k_scale and v_scale fp32 [R][Hkv].  Scales are
+ *   finite and >= 0 (an amax / 448 quantiser gives that); a zero scale is a
+ *   block of zeros whatever its codes (its keys keep their softmax share and
+ *   add nothing to the output).  Negative or non-finite scales are outside
+ *   the contract: the device cannot report them, and the output is then
+ *   unspecified (no memory is accessed out of bounds).
  * block_idx / block_cnt as produced by stem_schedule_topk (k_cap = its row
  *   stride; entries must be ascending, in [0, I]).
  * out: bf16 [T][Hq][d].  lse: optional fp32 [Hq][T] (natural log), may be NULL.
  * workspace: see stem_attn_workspace_bytes (STEM_ERR_WORKSPACE if too small).
  * Precision: Q.K^T in the input type (bf16, or e4m3 with fp32 scales), fp32
  * accumulation and softmax; P.V with P rounded to fp16 against an exact fp16
- * copy of V for bf16 inputs (V magnitudes above 65504 saturate), and to e4m3
- * for fp8 inputs (each weight times the block's V scale, relative to a running
- * reference that keeps the largest weight between 152 and 430, below e4m3's
- * 448), except in the diagonal block, which uses fp16.
+ * copy of V for bf16 inputs (V magnitudes above 65504 saturate to +-65504:
+ * such inputs are outside the bf16 contract), and to e4m3 for fp8 inputs
+ * (each weight times the block's V scale, relative to a running reference
+ * that keeps the largest weight between 152 and 430, below e4m3's 448),
+ * except in the diagonal block, which uses fp16.  An e4m3 weight is off by up
+ * to 2^-4 of itself; that averages out over many keys of similar weight but
+ * not when a few keys hold a query's attention, so for every 32 queries a
+ * block in which some query's largest weight exceeds 1/8 of that query's
+ * weight sum so far gets a second e4m3 P.V pass with the rounding residuals
+ * (about 2^-8 per weight in all).  On the synthetic workloads and on
+ * concentrated attention (logits scaled up to 8x) the fp8 output stays within
+ * max-abs 6e-2 of exact attention on the dequantised inputs.
  * ------------------------------------------------------------------------- */
 int stem_bsa_prefill(const stem_problem_t *p, int32_t dtype, const void *q, const void *k,
                      const void *v, const float *q_scale, const float *k_scale,
@@ -220,8 +233,14 @@ int stem_bsa_prefill(const stem_problem_t *p, int32_t dtype, const void *q, cons
  * ------------------------------------------------------------------------- */
 
 /* ---------------------------------------------------------------------------
- * Dense causal attention with the same tile kernel (every causal block).
- * Same arguments and outputs as stem_bsa_prefill without the lists.
+ * Dense causal attention with the same tile kernel (every causal block): the
+ * baseline of the AngelSlim doc §2.3 (its bf16 dense prefill, next to the
+ * fp8 block-sparse one) and of the §3 support table's dense entries; every
+ * speed-up of the sparse path is measured against it.
+ * out[t][h] = sum_{u <= t} softmax_u(softmax_scale * q_t.k_u) v_u per
+ * sequence (keys of earlier sequences never attend).  Same arguments, layout,
+ * precision and errors as stem_bsa_prefill without the lists; equal to
+ * stem_bsa_prefill with every causal block listed, bit for bit.
  * ------------------------------------------------------------------------- */
 int stem_dense_prefill(const stem_problem_t *p, int32_t dtype, const void *q, const void *k,
                        const void *v, const float *q_scale, const float *k_scale,

@@ -4,14 +4,14 @@ every block, or never), and uniform attention.  Attention runs on fixed lists
 (every causal block, and random ascending lists) so only the attention
 arithmetic is tested.
 
-bf16 meets the usual output bar on all of them.  For e4m3 the weights P are
-rounded to e4m3 before P.V (3 mantissa bits, relative error at most 2^-4) and
-the row sum uses the unrounded weights, so the output error is bounded by
-2^-4 * max|v| over the row's keys, which the flat logits of the workload
-inputs average far below the 6e-2 bar but peaked logits do not; those cases
-are checked against that bound.  With fp16_weights (dtype FP8_E4M3_PV16) every
-block's P.V uses fp16 weights, and e4m3 inputs meet the bf16 output bar on
-the same peaked logits.
+bf16 meets the bf16 output bar on all of them, and e4m3 inputs meet the fp8
+bar (max-abs 6e-2) on all of them with the default e4m3 weights: the kernel
+rounds P to e4m3 only in blocks where no key holds a large share of a
+query's attention, and runs the others with fp16 weights.  The gains 1.25 to
+1.75 put a handful of keys at 10-40 % of a row's weight each, the regime in
+which e4m3 weights would not average out.  With fp16_weights (dtype
+FP8_E4M3_PV16) every block uses fp16 weights, and e4m3 inputs meet the bf16
+output bar.
 """
 import math
 
@@ -22,7 +22,7 @@ import torch
 import block_sparse_attention_stem_amd as stem
 import oracle as O
 import stem_synth as S
-from gpu_common import (BF16_MAX_ABS, BF16_MEAN_REL, FP8_MAX_ABS, bf16_half_ulp, check_lse, check_out,
+from gpu_common import (BF16_MAX_ABS, BF16_MEAN_REL, FP8_MAX_ABS, check_lse, check_out,
                         check_scores, dequant, dev, f64, lists_equal, note, quantize_fp8, random_q64_lists,
                         to_dev)
 
@@ -34,7 +34,8 @@ HQ, HKV = 4, 2
 
 
 def _scaled(gain, seed=3):
-    """make_qkv with Q and K multiplied by `gain` (a power of two: exact in bf16)."""
+    """make_qkv with Q and K multiplied by `gain`, rounded to bf16 (both sides
+    see the same rounded values)."""
     q, k, v = S.make_qkv(LENS, HQ, HKV, 128, seed, True)
     return (q.float() * gain).to(torch.bfloat16), (k.float() * gain).to(torch.bfloat16), v
 
@@ -92,35 +93,20 @@ def _run_bf16(q, k, v, idx, cnt, where):
     check_lse(lse.cpu().numpy().astype(np.float64), rl, where)
 
 
-def _fp8_bound(vf, cu):
-    """[T][Hq] bound 2^-4 * max |v| over the causal keys of each query (any list)."""
-    T = vf.shape[0]
-    b = np.zeros((T, HQ))
-    for a, e in zip(cu[:-1], cu[1:]):
-        run = np.maximum.accumulate(np.abs(vf[a:e]).max(axis=2), axis=0)       # [L][Hkv]
-        for h in range(HQ):
-            b[a:e, h] = run[:, h // (HQ // HKV)] / 16.0
-    return b
-
-
-def _run_fp8(q, k, v, idx, cnt, where, peaked):
+def _run_fp8(q, k, v, idx, cnt, where, check_lse_too=True, v_scale_edit=None):
     cu = S.cu_from_lengths(LENS)
     p = stem.Problem(cu, HQ, HKV)
     (q8, k8, v8), (qs, ks, vs) = quantize_fp8(q, k, v, LENS)
+    if v_scale_edit is not None:
+        v_scale_edit(vs)
     qf, kf, vf = dequant(q8, qs), dequant(k8, ks), dequant(v8, vs)
     out, lse = stem.stem_bsa_prefill(p, *to_dev(q8, k8, v8), torch.from_numpy(idx).to(dev()),
                                      torch.from_numpy(cnt).to(dev()), SCALE, scales=to_dev(qs, ks, vs),
                                      want_lse=True)
     ro, rl = O.block_sparse_attention(qf, kf, vf, idx, cnt, cu, HQ, HKV, SCALE)
-    g = f64(out)
-    if not peaked:
-        check_out(g, ro, FP8_MAX_ABS, None, where)
+    check_out(f64(out), ro, FP8_MAX_ABS, None, where)
+    if check_lse_too:
         check_lse(lse.cpu().numpy().astype(np.float64), rl, where)
-        return
-    bound = _fp8_bound(vf, cu)[:, :, None] + bf16_half_ulp(ro)
-    worst = float((np.abs(g - ro) / bound).max())
-    note(f"  out {where}: max-abs {np.abs(g - ro).max():.3e}, worst error / (2^-4 max|v| + half ulp) {worst:.3f}")
-    assert worst <= 1.0, where
 
 
 @pytest.mark.parametrize("gain", [2, 4, 8])
@@ -146,21 +132,40 @@ def test_uniform_attention_is_the_causal_mean():
     q = torch.zeros(sum(LENS), HQ, 128, dtype=torch.bfloat16)
     idx, cnt = _lists("all", S.cu_from_lengths(LENS))
     _run_bf16(q, k, v, idx, cnt, "bf16 uniform")
-    _run_fp8(q, k, v, idx, cnt, "fp8 uniform", peaked=False)
+    _run_fp8(q, k, v, idx, cnt, "fp8 uniform")
 
 
-@pytest.mark.parametrize("gain", [2, 4])
-def test_fp8_peaked_logits_within_e4m3_weight_bound(gain):
+@pytest.mark.parametrize("gain", [1.25, 1.5, 1.75, 2, 4, 8])
+@pytest.mark.parametrize("kind", ["all", "random"])
+def test_fp8_peaked_logits(gain, kind):
+    """The default e4m3 path on concentrated attention, against the fp8 bar.
+    The LSE is checked up to gain 2 (see the fp16-weight test below)."""
     q, k, v = _scaled(gain)
-    idx, cnt = _lists("random", S.cu_from_lengths(LENS))
-    _run_fp8(q, k, v, idx, cnt, f"fp8 gain {gain}", peaked=True)
+    idx, cnt = _lists(kind, S.cu_from_lengths(LENS))
+    _run_fp8(q, k, v, idx, cnt, f"fp8 gain {gain} {kind}", check_lse_too=gain <= 2)
 
 
 @pytest.mark.parametrize("slope", [12.0, -12.0])
 def test_fp8_block_maxima_ramps(slope):
     q, k, v = _ramp(slope)
     idx, cnt = _lists("all", S.cu_from_lengths(LENS))
-    _run_fp8(q, k, v, idx, cnt, f"fp8 ramp {slope:+.0f}", peaked=True)
+    _run_fp8(q, k, v, idx, cnt, f"fp8 ramp {slope:+.0f}", check_lse_too=False)
+
+
+def test_fp8_zero_v_scale_blocks():
+    """A zero V scale is a block of zeros whatever its codes: its keys still
+    take their share of the softmax and contribute nothing to the output.
+    Zeroed: the first block of the first sequence (the first block of every
+    list there, and the only one of its first row) and a middle block of the
+    third, with their nonzero codes left in place."""
+    q, k, v = _scaled(1)
+
+    def edit(vs):
+        vs[0, 1] = 0.0
+        vs[2 + 6 + 4, 0] = 0.0
+    for kind in ("all", "random"):
+        idx, cnt = _lists(kind, S.cu_from_lengths(LENS))
+        _run_fp8(q, k, v, idx, cnt, f"fp8 zero v-scale {kind}", v_scale_edit=edit)
 
 
 @pytest.mark.parametrize("gain", [1, 2, 4])
@@ -219,3 +224,27 @@ def test_scores_with_all_zero_blocks():
         idx, cnt = stem.stem_schedule_topk(p, sc, ks_, mu, alpha, 1, 1)
         ri, rc = O.schedule_topk(sc.cpu().numpy(), cu, ks_, mu, alpha, 1, 1, idx.shape[2])
         lists_equal(idx.cpu().numpy(), cnt.cpu().numpy(), ri, rc, f"zero blocks, {tag} scoring")
+
+
+def test_bf16_values_beyond_fp16_range_saturate():
+    """bf16 P.V runs against an fp16 copy of V, so V entries beyond fp16's
+    range (|v| > 65504) are taken as +-65504, as the header states: the output
+    equals exact attention on V clamped to +-65504 (the bf16 bar), and differs
+    from exact attention on the unclamped V.  Such inputs are outside the bf16
+    contract; this pins what the library does with them."""
+    q, k, v = _scaled(1)
+    v = v.float()
+    v[256 + 128:256 + 160, 1, :8] = 2.0e5            # a few huge entries in one block of KV head 1
+    v[256 + 768 + 300, 0, 3] = -1.0e6
+    v = v.to(torch.bfloat16)
+    assert float(v.float().abs().max()) > 65504
+    cu = S.cu_from_lengths(LENS)
+    p = stem.Problem(cu, HQ, HKV)
+    idx, cnt = _lists("all", cu)
+    out = stem.stem_bsa_prefill(p, *to_dev(q, k, v), torch.from_numpy(idx).to(dev()),
+                                torch.from_numpy(cnt).to(dev()), SCALE)
+    vc = np.clip(f64(v), -65504.0, 65504.0)
+    ro, _ = O.block_sparse_attention(f64(q), f64(k), vc, idx, cnt, cu, HQ, HKV, SCALE)
+    check_out(f64(out), ro, BF16_MAX_ABS, BF16_MEAN_REL, "bf16 V beyond fp16 range, against clamped V")
+    raw, _ = O.block_sparse_attention(f64(q), f64(k), f64(v), idx, cnt, cu, HQ, HKV, SCALE)
+    assert float(np.abs(f64(out) - raw).max()) > 1.0

@@ -1,5 +1,5 @@
 """GPU parity at the full workload sizes: 32K and 128K bf16 layers and the
-128K fp8 varlen layer.
+128K fp8 varlen layer at both alpha values of its layer schedule (1.0 and 0.7).
 
 The GPU runs every stage on the whole workload through the C ABI, with the
 entry points, arguments and preallocated workspaces the benchmark times.
@@ -144,10 +144,11 @@ def _run(w, fp8):
     return res
 
 
-@pytest.fixture(scope="module", params=["n32k_32q8kv", "n128k_32q8kv", "fp8_layer5"])
+@pytest.fixture(scope="module", params=["n32k_32q8kv", "n128k_32q8kv", "fp8_layer0", "fp8_layer5"])
 def big(request):
-    if request.param == "fp8_layer5":
-        return _run(S.fp8_workload(5), fp8=True)
+    # fp8 layers 0-4 of the 36-layer schedule use alpha 1.0, layers 5-35 alpha 0.7
+    if request.param.startswith("fp8_layer"):
+        return _run(S.fp8_workload(int(request.param[len("fp8_layer"):])), fp8=True)
     return _run(S.CONFIGS[request.param], fp8=False)
 
 

@@ -222,6 +222,14 @@ def test_topk_tie_stress():
         idx, cnt = stem.stem_schedule_topk(p, sc.to(dev()), ks, 0.6, 1.0, 1, 1)
         ri, rc = O.schedule_topk(sc.numpy(), cu, ks, 0.6, 1.0, 1, 1, idx.shape[2])
         lists_equal(idx.cpu().numpy(), cnt.cpu().numpy(), ri, rc, f"ties={ties}")
+    # -0.0 and +0.0 are equal scores: half the zeros of a two-value draw get a minus sign
+    sc = S.random_scores_like(4, lens, ties=2, seed=7)
+    flip = torch.rand(sc.shape, generator=torch.Generator().manual_seed(8)) < 0.5
+    sc = torch.where((sc == 0) & flip, torch.full_like(sc, -0.0), sc)
+    assert bool(torch.signbit(sc[sc == 0]).any()) and bool((~torch.signbit(sc[sc == 0])).any())
+    idx, cnt = stem.stem_schedule_topk(p, sc.to(dev()), [5, 4], 0.6, 1.0, 1, 1)
+    ri, rc = O.schedule_topk(sc.numpy(), cu, [5, 4], 0.6, 1.0, 1, 1, idx.shape[2])
+    lists_equal(idx.cpu().numpy(), cnt.cpu().numpy(), ri, rc, "signed zeros")
 
 
 # ---------------------------------------------------------------- fp8 --------

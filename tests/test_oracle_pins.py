@@ -7,6 +7,7 @@ to a textbook quantity, an invariant, a library routine, or a hand example.
 import itertools
 import json
 import math
+from fractions import Fraction
 import os
 
 import numpy as np
@@ -490,3 +491,53 @@ def test_varlen_packing_equals_separate_sequences():
         assert np.array_equal(Sp[:, r0:r0 + nb, :nb], Sz[:, :, :nb])
         assert np.all(Sp[:, r0:r0 + nb, nb:] == -np.inf)
         r0 += nb
+
+
+def _kept_closed_form(I, nb, k_start, mu, alpha, n_init, n_window):
+    """gist.science Stem summary §2.1 budget, written out with exact rationals:
+    floor(ke - ke (1 - mu) I / nb), ke = alpha k_start, then at least the
+    forced blocks and at most the I + 1 causal ones."""
+    ke = Fraction(str(alpha)) * Fraction(str(k_start))
+    k = math.floor(ke - ke * (1 - Fraction(str(mu))) * Fraction(I, nb))
+    forced = len(set(range(min(n_init, I + 1))) | set(range(max(0, I - n_window + 1), I + 1)))
+    return min(I + 1, max(k, forced))
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_schedule_topk_packed_batch_equals_separate_sequences(seed):
+    """A packed batch is scheduled row by row exactly as each sequence alone:
+    sequence z uses its own k_start[z] and block count, and its rows sit at
+    global rows r0(z) .. r0(z) + nb_z - 1.  Every row's count is the closed
+    form above, every list is ascending, causal and holds the forced blocks."""
+    lens = (384, 1024, 128, 768)
+    k_start = [2, 5, 1, 4]
+    mu, alpha, n_init, n_window = 0.6, 0.7, 1, 2
+    cu = S.cu_from_lengths(lens)
+    sc = S.random_scores_like(3, lens, ties=3 if seed == 1 else None, seed=seed).numpy()
+    k_cap = max(L // 128 for L in lens) + 2
+    idx, cnt = O.schedule_topk(sc, cu, k_start, mu, alpha, n_init, n_window, k_cap)
+    r0 = 0
+    for z, L in enumerate(lens):
+        nb = L // 128
+        iz, cz = O.schedule_topk(sc[:, r0:r0 + nb, :nb].copy(), [0, L], [k_start[z]], mu, alpha,
+                                 n_init, n_window, k_cap)
+        assert np.array_equal(idx[:, r0:r0 + nb], iz) and np.array_equal(cnt[:, r0:r0 + nb], cz)
+        for I in range(nb):
+            want = _kept_closed_form(I, nb, k_start[z], mu, alpha, n_init, n_window)
+            forced = set(range(min(n_init, I + 1))) | set(range(max(0, I - n_window + 1), I + 1))
+            for h in range(3):
+                row = idx[h, r0 + I, :cnt[h, r0 + I]].tolist()
+                assert cnt[h, r0 + I] == want
+                assert row == sorted(set(row)) and all(0 <= J <= I for J in row)
+                assert forced <= set(row)
+                assert np.all(idx[h, r0 + I, cnt[h, r0 + I]:] == -1)
+        r0 += nb
+
+
+def test_signed_zero_scores_tie():
+    """-0.0 and +0.0 are equal scores: the lower block index wins either way."""
+    row = np.array([1.0, -0.0, 0.0, -0.0, 0.0, -1.0], dtype=np.float32)
+    for kept, want in ((2, [0, 1]), (3, [0, 1, 2]), (4, [0, 1, 2, 3])):
+        assert O.select_row(row, 5, kept, []) == want
+    row2 = np.array([0.0, -0.0, 0.0, 2.0], dtype=np.float32)
+    assert O.select_row(row2, 3, 2, []) == [0, 3]
