@@ -22,7 +22,7 @@ import torch
 import block_sparse_attention_stem_amd as stem
 import oracle as O
 import stem_synth as S
-from gpu_common import (BF16_MAX_ABS, BF16_MEAN_REL, FP8_MAX_ABS, check_lse, check_out,
+from gpu_common import (BF16_MAX_ABS, BF16_MEAN_REL, FP8_MAX_ABS, bf16_half_ulp, check_lse, check_out,
                         check_scores, dequant, dev, f64, lists_equal, note, quantize_fp8, random_q64_lists,
                         to_dev)
 
@@ -245,6 +245,16 @@ def test_bf16_values_beyond_fp16_range_saturate():
                                 torch.from_numpy(cnt).to(dev()), SCALE)
     vc = np.clip(f64(v), -65504.0, 65504.0)
     ro, _ = O.block_sparse_attention(f64(q), f64(k), vc, idx, cnt, cu, HQ, HKV, SCALE)
-    check_out(f64(out), ro, BF16_MAX_ABS, BF16_MEAN_REL, "bf16 V beyond fp16 range, against clamped V")
+    # With |v| up to 65504 an absolute bar means nothing: the fp16 weights
+    # carry up to 2^-11 of relative error each, so the bound scales with
+    # sum_k w_k |v_k| (the same attention on |v|); 2^-10 leaves a factor 2.
+    ra, _ = O.block_sparse_attention(f64(q), f64(k), np.abs(vc), idx, cnt, cu, HQ, HKV, SCALE)
+    g = f64(out)
+    err = np.abs(g - ro)
+    bound = BF16_MAX_ABS + 2.0 ** -10 * ra + bf16_half_ulp(ro)
+    note(f"  out bf16 V beyond fp16 range: max |d| {err.max():.3e}, worst |d| / bound {(err / bound).max():.3f}")
+    assert float((err / bound).max()) <= 1.0
+    d = np.abs(g - ro).mean() / np.abs(ro).mean()
+    assert d <= BF16_MEAN_REL, d
     raw, _ = O.block_sparse_attention(f64(q), f64(k), f64(v), idx, cnt, cu, HQ, HKV, SCALE)
-    assert float(np.abs(f64(out) - raw).max()) > 1.0
+    assert float(np.abs(g - raw).max()) > 1000.0          # the unclamped values would differ a lot
