@@ -45,6 +45,7 @@ DEFAULTS = dict(block_size=128, stride=8, chunk_size=2048, norm=1.0,
                 initial_blocks=4, window_size=4, stem_alpha=1.0, beta=0.2)
 
 EXPORTED = ("stem_status_string", "stem_score_workspace_bytes", "stem_score", "stem_score_fp8",
+            "stem_score_noalloc",
             "stem_schedule_topk", "stem_tpd_budget", "stem_kept_count", "stem_max_kept",
             "stem_attn_workspace_bytes", "stem_bsa_prefill", "stem_dense_prefill",
             "stem_bsa_prefill_paged", "stem_bsa_prefill_q64")
@@ -84,6 +85,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.stem_score_workspace_bytes.restype = sz
     lib.stem_score.argtypes = [P, vp, vp, vp, i32, i32, f32, f32, vp, vp, sz, vp]
     lib.stem_score.restype = ctypes.c_int
+    lib.stem_score_noalloc.argtypes = [P, vp, vp, vp, i32, i32, f32, f32, vp, vp]
+    lib.stem_score_noalloc.restype = ctypes.c_int
     lib.stem_score_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, i32, f32, f32, vp, vp, sz, vp]
     lib.stem_score_fp8.restype = ctypes.c_int
     lib.stem_schedule_topk.argtypes = [P, vp, ctypes.POINTER(f64), f64, f64, i32, i32, i32, vp, vp, vp]
@@ -200,6 +203,24 @@ def stem_score(p: Problem, q, k, v, stride: int = 8, chunk_size: int = 2048, nor
         _check("stem_score", st)
     if own_ws:
         _on_stream(workspace, stream)
+    return scores
+
+
+STEM_SCORE_SCRATCH_BYTES = 1 << 20      # the library's own scratch per GPU (stem_score_noalloc)
+
+
+def stem_score_noalloc(p: Problem, q, k, v, scores: torch.Tensor, stride: int = 8, chunk_size: int = 2048,
+                       norm: float = 1.0, beta: float = 0.2, stream=None) -> torch.Tensor:
+    """stem_score without a workspace: the library's own device scratch array
+    stands in for it, and nothing is allocated here either (`scores` must be
+    preallocated fp32 [Hq][R][max_nb]).  Calls that overlap on one GPU race."""
+    lib = load_library()
+    for name, t, h in (("q", q, p.Hq), ("k", k, p.Hkv), ("v", v, p.Hkv)):
+        _need(t, name, torch.bfloat16, (p.T, h, p.d))
+    _need(scores, "scores", torch.float32, (p.Hq, p.R, p.max_nb))
+    st = lib.stem_score_noalloc(p.ref, _ptr(q), _ptr(k), _ptr(v), stride, chunk_size, float(norm), float(beta),
+                                _ptr(scores), _stream(stream))
+    _check("stem_score_noalloc", st)
     return scores
 
 

@@ -8,6 +8,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 using namespace stem;
 
 namespace {
@@ -147,6 +149,46 @@ static int score_common(const stem_problem_t *p, const void *q, const void *k, c
 }
 
 
+// ------------------------------------------------------------ no-alloc path
+// stem_score_noalloc uses this file-scope device array in place of the
+// caller's score workspace.  Each GPU the library runs on holds its own copy
+// (at its own address) until the process ends.  In host code the name
+// `scratch` is only a stand-in for the symbol: its device address is looked up
+// once per device with hipGetSymbolAddress, with that device current, and
+// only that address is ever passed to a kernel.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[STEM_SCORE_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];    // device address of `scratch` per device, null until resolved
+
+// The device `stream` launches on (the current device for the null stream),
+// and that device's address of `scratch`, resolved on first use.
+int scratch_for_stream(hipStream_t stream, void **out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return STEM_ERR_HIP;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t d = 0;
+    if (hipStreamGetDevice(stream, &d) != hipSuccess) return STEM_ERR_HIP;
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return STEM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return STEM_ERR_HIP;
+    void *ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !ptr || ((uintptr_t)ptr & 255u)) return STEM_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return STEM_OK;
+}
+}  // namespace
+
 extern "C" {
 
 int stem_score(const stem_problem_t *p, const void *q, const void *k, const void *v,
@@ -154,6 +196,21 @@ int stem_score(const stem_problem_t *p, const void *q, const void *k, const void
                void *workspace, size_t workspace_bytes, void *stream) {
   return score_common(p, q, k, v, nullptr, nullptr, nullptr, false, stride, chunk_size, norm, beta, scores,
                       workspace, workspace_bytes, stream);
+}
+
+int stem_score_noalloc(const stem_problem_t *p, const void *q, const void *k, const void *v,
+                       int32_t stride, int32_t chunk_size, float norm, float beta, float *scores,
+                       void *stream) {
+  // the size check comes first, so an oversized problem never touches the device
+  Shape s;
+  const int st = check_problem(p, &s);
+  if (st != STEM_OK) return st;
+  if (stem_score_workspace_bytes(p) > (size_t)STEM_SCORE_SCRATCH_BYTES) return STEM_ERR_WORKSPACE;
+  void *ptr = nullptr;
+  const int sr = scratch_for_stream(as_stream(stream), &ptr);
+  if (sr != STEM_OK) return sr;
+  return score_common(p, q, k, v, nullptr, nullptr, nullptr, false, stride, chunk_size, norm, beta, scores, ptr,
+                      (size_t)STEM_SCORE_SCRATCH_BYTES, stream);
 }
 
 int stem_score_fp8(const stem_problem_t *p, const void *q, const void *k, const void *v,

@@ -113,6 +113,25 @@ int stem_score(const stem_problem_t *p, const void *q, const void *k, const void
                int32_t stride, int32_t chunk_size, float norm, float beta,
                float *scores, void *workspace, size_t workspace_bytes, void *stream);
 
+/* stem_score for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same computation and result as stem_score, with the library's own device
+ * array of STEM_SCORE_SCRATCH_BYTES (1 MiB, one per GPU, held until the
+ * process ends) in place of the workspace argument: enough for
+ * num_kv_heads * R <= 262144 (e.g. 8 KV heads and 4M tokens).  Larger
+ * problems return STEM_ERR_WORKSPACE before anything is enqueued.  The call
+ * allocates nothing; its first call on a GPU (the device of `stream`, or the
+ * current device for the null stream) looks up that GPU's array address
+ * (hipGetSymbolAddress), so a caller that will capture should make one call
+ * on that device beforehand.  Every call on a GPU uses that GPU's one array:
+ * calls that overlap on one GPU (different streams, threads or graphs in
+ * flight together) race and must be serialised by the caller.  The array's
+ * contents are rewritten by every call before they are read. */
+#define STEM_SCORE_SCRATCH_BYTES (1u << 20)
+int stem_score_noalloc(const stem_problem_t *p, const void *q, const void *k, const void *v,
+                       int32_t stride, int32_t chunk_size, float norm, float beta,
+                       float *scores, void *stream);
+
 /* Stage 1 on e4m3 inputs: the scores above, with Q, K and V the dequantised
  * values code * scale (the e4m3 layout of stem_bsa_prefill: codes [T][H][d],
  * fp32 scales [R][H] per (128-token block, head), all device memory).  The

@@ -255,3 +255,20 @@ int main(void) {
                     str(src), "-o", str(exe), "-L", lib_dir, "-lstem", "-Wl,-rpath," + lib_dir], check=True)
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert r.returncode == 0 and r.stdout.strip() == "ok", (r.returncode, r.stdout, r.stderr)
+
+
+def test_noalloc_score_rejects_problems_beyond_its_scratch():
+    """stem_score_noalloc checks the problem against its fixed scratch array
+    before touching the device: Hkv * R floats must fit in
+    STEM_SCORE_SCRATCH_BYTES, else STEM_ERR_WORKSPACE (no launch, no GPU)."""
+    lib = stem.load_library()
+    assert stem.STEM_SCORE_SCRATCH_BYTES == 1 << 20
+    dummy = ctypes.c_void_p(256)
+    for Hkv, nblk, ok in ((64, 4097, False), (8, 32769, False)):
+        p = stem.Problem([0, 128 * nblk], Hkv, Hkv)
+        assert Hkv * nblk * 4 > stem.STEM_SCORE_SCRATCH_BYTES
+        st = lib.stem_score_noalloc(p.ref, dummy, dummy, dummy, 8, 2048, 1.0, 0.2, dummy, None)
+        assert st == 4, stem.STATUS.get(st, st)                  # STEM_ERR_WORKSPACE
+    # invalid problems are rejected as in stem_score
+    p = stem.Problem([0, 100], 2, 1)
+    assert lib.stem_score_noalloc(p.ref, dummy, dummy, dummy, 8, 2048, 1.0, 0.2, dummy, None) == 2
