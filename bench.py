@@ -8,13 +8,15 @@ default workload is the 128K-token Qwen3-8B-shaped layer (32 query heads, 8
 KV heads, d = 128) at ~25 % kept block pairs, timed against the library's own
 dense causal attention on the same inputs.
 
-    python bench.py [--steps K] [--warmup W] [--no-sweep] [--no-fp8] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--no-sweep] [--no-length-sweep] [--no-fp8]
+                    [--no-cpu-baseline]
 
 Prints ONE JSON line.  value = effective TFLOP/s = dense-equivalent causal
 attention FLOP (4 d Hq sum_z L_z (L_z + 1) / 2) / Stem end-to-end time.
 Besides the headline layer it reports the density sweep at 64K (linearity
-and skip overhead), the fp8 varlen batch (four packed sequences, 128K
-tokens, per-layer times and the 36-layer alpha schedule) and the CPU
+and skip overhead), the length sweep 2K..256K (Stem vs dense, crossover),
+the fp8 varlen batch (four packed sequences, 128K tokens, per-layer times
+and the 36-layer alpha schedule run on fresh inputs per layer) and the CPU
 oracle's rate on a bounded sample.
 """
 from __future__ import annotations
@@ -389,13 +391,18 @@ def run_main(args):
     log(f"[bench] reference bf16 GEMM (torch.mm, 16384^3, N(0,1) operands): "
         f"{res['reference_bf16_gemm']['tflops']:.0f} TFLOP/s")
 
+    idx_cpu, cnt_cpu = idx.cpu(), cnt.cpu()       # the lists, for the CPU baseline
+    del qd, kd, vd, scores, ws, idx, cnt, out, dout, aws
+    torch.cuda.empty_cache()
     if not args.no_sweep:
         res["density_sweep"] = density_sweep(args, torch, stem, S, dev)
+    if not args.no_length_sweep:
+        res["length_sweep"] = length_sweep(args, torch, stem, S, dev)
     if not args.no_fp8:
         res["fp8_varlen"] = fp8_varlen(args, torch, stem, S, dev)
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle, bounded sample)")
-        res["cpu_baseline"] = cpu_baseline(w, q, k, v, idx, cnt, flop_dense)
+        res["cpu_baseline"] = cpu_baseline(w, q, k, v, idx_cpu, cnt_cpu, flop_dense)
     print(json.dumps(res), flush=True)
 
 
@@ -501,16 +508,83 @@ def fp8_varlen(args, torch, stem, S, dev):
                                 "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s", "frac": s_tflops / PEAK_FP8_TFLOPS}}
     log(f"[bench]   fp8 scoring: {t_s8:.2f} ms vs {t_s16:.2f} ms on bf16 (alternating); "
         f"36 layers {total8:.1f} ms ({36 * t_dense / total8:.2f}x dense)")
+    del scores, scores8, ws, aws, out, qd, kd, vd, qa, ka, va, kpd, vpd, tabd
+    torch.cuda.empty_cache()
+    run36 = run_36_layers(torch, stem, S, dev)
+    fp8_scoring["ms_36_layers_derived"] = fp8_scoring.pop("ms_36_layers")
+    fp8_scoring["speedup_vs_dense_36_layers_derived"] = fp8_scoring.pop("speedup_vs_dense_36_layers")
+    fp8_scoring["ms_36_layers"] = run36["ms_e4m3_scoring"]
+    fp8_scoring["speedup_vs_dense_36_layers"] = run36["speedup_vs_dense_e4m3_scoring"]
     return {"workload": "fp8 e4m3 varlen, seqlens 8192/16384/32768/73728 (T=131072), 32q/8kv, "
                         "d128, per-(128-block, head) scales, k_start 18/35/70/156, mu 0.5, 1 sink + 2 window",
             "layers": layers, "dense_ms": t_dense,
             "dense_tflops": flop_dense / (t_dense * 1e-3) / 1e12,
-            "ms_36_layers": total, "dense_ms_36_layers": 36 * t_dense,
-            "speedup_vs_dense_36_layers": 36 * t_dense / total,
+            "ms_36_layers": run36["ms"], "dense_ms_36_layers": run36["dense_ms"],
+            "speedup_vs_dense_36_layers": run36["speedup_vs_dense"],
+            "ms_36_layers_derived": total, "dense_ms_36_layers_derived": 36 * t_dense,
+            "run_36_layers": run36,
             "fp8_scoring": fp8_scoring,
             "roofline": {"bound": "mfma", "kernel": "attn_fp8_kernel<sparse>", "achieved": lo["bsa_tflops"],
                          "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                          "frac": lo["bsa_tflops"] / PEAK_FP8_TFLOPS}}
+
+
+def run_36_layers(torch, stem, S, dev):
+    """The fp8 varlen batch over the 36-layer alpha schedule ([1.0] x 5 +
+    [0.7] x 31), each layer with fresh Q/K/V (seed = layer index, drawn on the
+    GPU outside the timed calls) and its own scores and lists.  Every layer is
+    run once per path and timed with HIP events per call: Stem with bf16
+    scoring (score + schedule + e4m3 attention), Stem with scoring on the e4m3
+    codes (stem_score_fp8 + schedule on its scores + e4m3 attention), and the
+    dense e4m3 kernel."""
+    w0 = S.fp8_workload(0)
+    p = stem.Problem(w0.cu_seqlens, w0.num_q_heads, w0.num_kv_heads)
+    scores = torch.empty((p.Hq, p.R, p.max_nb), dtype=torch.float32, device=dev)
+    ws = torch.empty(stem.stem_score_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    aws = torch.empty(stem.stem_attn_workspace_bytes(p, stem.STEM_DTYPE_FP8_E4M3), dtype=torch.uint8, device=dev)
+    out = torch.empty((p.T, p.Hq, 128), dtype=torch.bfloat16, device=dev)
+    kcap = max(stem.stem_max_kept(p, S.fp8_workload(l).k_start, w0.mu, S.FP8_ALPHAS[l], w0.n_init, w0.n_window)
+               for l in range(len(S.FP8_ALPHAS)))
+    idx = torch.empty((p.Hq, p.R, kcap), dtype=torch.int32, device=dev)
+    cnt = torch.empty((p.Hq, p.R), dtype=torch.int32, device=dev)
+    rows = []
+    for layer in range(len(S.FP8_ALPHAS)):
+        w = S.fp8_workload(layer)
+        q, k, v = S.make_workload_qkv(w, device=str(dev))
+        (q8, qs), (k8, ks), (v8, vs) = (S.quantize_e4m3_per_block(t, w.seqlens) for t in (q, k, v))
+        sc = (qs, ks, vs)
+        calls = [
+            ("score", lambda: stem.stem_score(p, q, k, v, w.stride, w.chunk_size, w.norm, w.beta, scores, ws)),
+            ("schedule", lambda: stem.stem_schedule_topk(p, scores, w.k_start, w.mu, w.alpha, w.n_init,
+                                                         w.n_window, kcap, idx, cnt)),
+            ("bsa", lambda: stem.stem_bsa_prefill(p, q8, k8, v8, idx, cnt, scales=sc, out=out, workspace=aws)),
+            ("score_fp8", lambda: stem.stem_score(p, q8, k8, v8, w.stride, w.chunk_size, w.norm, w.beta, scores,
+                                                  ws, scales=sc)),
+            ("schedule_fp8", lambda: stem.stem_schedule_topk(p, scores, w.k_start, w.mu, w.alpha, w.n_init,
+                                                             w.n_window, kcap, idx, cnt)),
+            ("bsa_fp8", lambda: stem.stem_bsa_prefill(p, q8, k8, v8, idx, cnt, scales=sc, out=out, workspace=aws)),
+            ("dense", lambda: stem.stem_dense_prefill(p, q8, k8, v8, scales=sc, out=out, workspace=aws)),
+        ]
+        if layer == 0:                     # warm every call once on the first layer's inputs
+            for _, fn in calls:
+                fn()
+            torch.cuda.synchronize()
+        timer = StageTimer(torch, [n for n, _ in calls])
+        ev = timer.run([fn for _, fn in calls])
+        torch.cuda.synchronize()
+        timer.collect(ev)
+        rows.append({n: timer.mean(n) for n, _ in calls})
+        del q, k, v, q8, k8, v8, sc
+    t_bf = [r["score"] + r["schedule"] + r["bsa"] for r in rows]
+    t_f8 = [r["score_fp8"] + r["schedule_fp8"] + r["bsa_fp8"] for r in rows]
+    t_dn = [r["dense"] for r in rows]
+    log(f"[bench]   fp8 36 layers (fresh inputs per layer): {sum(t_bf):.1f} ms with bf16 scoring, "
+        f"{sum(t_f8):.1f} ms with e4m3 scoring, dense {sum(t_dn):.1f} ms")
+    return {"data": "fresh Q/K/V per layer (seed = layer index), drawn on the GPU; every layer run once",
+            "alpha": list(S.FP8_ALPHAS), "ms": sum(t_bf), "ms_e4m3_scoring": sum(t_f8), "dense_ms": sum(t_dn),
+            "speedup_vs_dense": sum(t_dn) / sum(t_bf), "speedup_vs_dense_e4m3_scoring": sum(t_dn) / sum(t_f8),
+            "per_layer_ms": [round(x, 4) for x in t_bf], "per_layer_ms_e4m3_scoring": [round(x, 4) for x in t_f8],
+            "per_layer_dense_ms": [round(x, 4) for x in t_dn]}
 
 
 def page_pool(torch, k8, v8, ks, vs, seqlens, seed=0, spare=3):
@@ -563,17 +637,16 @@ def kstart_for_density(stem, nb, target, alpha=0.7, mu=0.5, n_init=1, n_window=2
 
 
 def length_sweep(args, torch, stem, S, dev):
-    """One layer (32 q / 8 kv heads, d 128) at 4K .. 256K tokens, ~25 % kept
+    """One layer (32 q / 8 kv heads, d 128) at 2K .. 256K tokens, ~25 % kept
     (alpha 0.7, mu 0.5, 1 sink + 2 window, k_start chosen per length with the
-    library's TPD rule): Stem (score + schedule + BSA) vs the dense kernel."""
+    library's TPD rule): Stem (score + schedule + BSA) vs the dense kernel.
+    Inputs are drawn on the GPU (seeded; the same recipe as the CPU draw)."""
     pts = []
-    for L in (4096, 8192, 16384, 32768, 65536, 131072, 262144):
+    for L in (2048, 4096, 8192, 16384, 32768, 65536, 131072, 262144):
         nb = L // 128
         ks = kstart_for_density(stem, nb, 0.25)
         log(f"[bench] length sweep: N={L}, k_start {ks}")
-        q, k, v = S.make_qkv((L,), 32, 8, 128, seed=0, sink=True)
-        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
-        del q, k, v
+        qd, kd, vd = S.make_qkv((L,), 32, 8, 128, seed=0, sink=True, device=str(dev))
         p = stem.Problem([0, L], 32, 8)
         scores = torch.empty((p.Hq, p.R, p.max_nb), dtype=torch.float32, device=dev)
         ws = torch.empty(stem.stem_score_workspace_bytes(p), dtype=torch.uint8, device=dev)
@@ -618,8 +691,9 @@ def length_sweep(args, torch, stem, S, dev):
             + f") dense {t_dense:.3f} ms -> {t_dense / t_stem:.2f}x")
         del qd, kd, vd, scores, ws, idx, cnt, out, aws
         torch.cuda.empty_cache()
+    cross = next((pt["seq_len"] for pt in pts if pt["speedup"] > 1.0), None)
     return {"workload": "one layer, 32q/8kv, d128, ~25% kept (alpha 0.7, mu 0.5, 1 sink + 2 window)",
-            "points": pts}
+            "points": pts, "first_length_faster_than_dense": cross}
 
 
 def density_sweep(args, torch, stem, S, dev):
@@ -684,6 +758,7 @@ def main():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--length-sweep", action="store_true",
                     help="only run the 4K..256K length sweep (Stem vs dense) and print its JSON")
+    ap.add_argument("--no-length-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 3 plain device-to-device copies of MIB MiB (to scale the "

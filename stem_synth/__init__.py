@@ -107,24 +107,29 @@ def fp8_workload(layer: int) -> Workload:
 
 def make_qkv(seqlens: Sequence[int], num_q_heads: int, num_kv_heads: int,
              head_dim: int = 128, seed: int = 0, sink: bool = True,
-             dtype: torch.dtype = torch.bfloat16):
-    """Draw Q, K, V token-major ([T][H][d]) on the CPU.
+             dtype: torch.dtype = torch.bfloat16, device: str = "cpu"):
+    """Draw Q, K, V token-major ([T][H][d]).
 
     Recipe: Q, K, V ~ N(0, 1); each V row is rescaled by a lognormal(0, 0.5)
     norm factor; with `sink`, the first 256 keys of every sequence get a
     shared unit direction times 3 added (attention-sink structure).  Drawn in
     fp32 and rounded once to `dtype` (round-to-nearest-even).
+
+    The draw runs on `device` with a generator seeded there: the default CPU
+    draw gives the same bits on every machine (every parity test uses it); a
+    GPU draw has the same distribution but other bits, and serves timing runs
+    that need many large fresh layers quickly.
     """
     T = int(sum(seqlens))
-    g = torch.Generator(device="cpu")
+    g = torch.Generator(device=device)
     g.manual_seed(int(seed))
-    q = torch.randn(T, num_q_heads, head_dim, generator=g, dtype=torch.float32)
-    k = torch.randn(T, num_kv_heads, head_dim, generator=g, dtype=torch.float32)
-    v = torch.randn(T, num_kv_heads, head_dim, generator=g, dtype=torch.float32)
-    r = torch.exp(0.5 * torch.randn(T, num_kv_heads, generator=g, dtype=torch.float32))
+    q = torch.randn(T, num_q_heads, head_dim, generator=g, dtype=torch.float32, device=device)
+    k = torch.randn(T, num_kv_heads, head_dim, generator=g, dtype=torch.float32, device=device)
+    v = torch.randn(T, num_kv_heads, head_dim, generator=g, dtype=torch.float32, device=device)
+    r = torch.exp(0.5 * torch.randn(T, num_kv_heads, generator=g, dtype=torch.float32, device=device))
     v.mul_(r.unsqueeze(-1))
     if sink:
-        u = torch.randn(num_kv_heads, head_dim, generator=g, dtype=torch.float32)
+        u = torch.randn(num_kv_heads, head_dim, generator=g, dtype=torch.float32, device=device)
         u = u / u.norm(dim=-1, keepdim=True)
         start = 0
         for n in seqlens:
@@ -134,8 +139,8 @@ def make_qkv(seqlens: Sequence[int], num_q_heads: int, num_kv_heads: int,
     return q.to(dtype), k.to(dtype), v.to(dtype)
 
 
-def make_workload_qkv(w: Workload, dtype: torch.dtype = torch.bfloat16):
-    return make_qkv(w.seqlens, w.num_q_heads, w.num_kv_heads, w.head_dim, w.seed, w.sink, dtype)
+def make_workload_qkv(w: Workload, dtype: torch.dtype = torch.bfloat16, device: str = "cpu"):
+    return make_qkv(w.seqlens, w.num_q_heads, w.num_kv_heads, w.head_dim, w.seed, w.sink, dtype, device)
 
 
 def make_topic_qkv(seqlens: Sequence[int], num_q_heads: int, num_kv_heads: int,
