@@ -102,10 +102,13 @@ __device__ __forceinline__ int key_of_pos8(int pos) {
 // ================================================================ pre-pass
 // One workgroup per (global key block, KV head): V block -> LDS -> V^T image.
 __global__ __launch_bounds__(256) void vprep_bf16_kernel(const __bf16 *__restrict__ v,
-                                                         uint16_t *__restrict__ img, int Hkv, int R) {
+                                                         uint16_t *__restrict__ img, int Hkv, int R,
+                                                         int32_t *__restrict__ ctr, int n_ctr) {
   constexpr int RS = kHeadDim + 8;
   __shared__ __attribute__((aligned(16))) uint16_t tile[kBlock * RS];
   const int kb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  if (kb == 0 && g == 0)             // the attention kernel's work queues start empty
+    for (int i = tid; i < n_ctr; i += 256) ctr[i] = 0;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
     const int key = (tid >> 4) + 16 * p, ch = tid & 15;
@@ -217,9 +220,8 @@ struct AttnItem {
 // prefix) to the first, then by the G query heads of the group; each XCD
 // takes a contiguous eighth of that order (xcd_chunk_item), so its L2 serves
 // neighbouring rows of one KV group, which list mostly the same blocks.
-__device__ __forceinline__ AttnItem decode_attn(const AttnLaunch &a, const SeqTable &t, int rows) {
+__device__ __forceinline__ AttnItem decode_item(const AttnLaunch &a, const SeqTable &t, int rows, int item) {
   const int G = a.Hq / a.Hkv;
-  const int item = xcd_chunk_item(blockIdx.x, rows * a.Hq);
   const int slot = item / G, hh = item - slot * G;
   AttnItem w;
   w.g = slot / rows;
@@ -229,6 +231,9 @@ __device__ __forceinline__ AttnItem decode_attn(const AttnLaunch &a, const SeqTa
   w.z = seq_of(t.row, t.n, w.r);
   w.I = w.r - t.row[w.z];
   return w;
+}
+__device__ __forceinline__ AttnItem decode_attn(const AttnLaunch &a, const SeqTable &t, int rows) {
+  return decode_item(a, t, rows, xcd_chunk_item(blockIdx.x, rows * a.Hq));
 }
 
 __device__ __forceinline__ void write_out(__bf16 *orow, const f32x16 (&o)[4], float inv, int lg) {
@@ -241,6 +246,33 @@ __device__ __forceinline__ void write_out(__bf16 *orow, const f32x16 (&o)[4], fl
       v2[1] = pack_bf16x2(o[u][4 * jj + 2] * inv, o[u][4 * jj + 3] * inv);
       st8(orow + 32 * u + 8 * jj + 4 * lg, v2);
     }
+}
+
+// The output tile goes out through LDS: in the MFMA layout a lane holds one
+// query's dims in 8-byte pieces, and the query rows of [T][Hq][d] lie
+// Hq * d * 2 bytes apart, so direct stores would touch 32 rows per
+// instruction.  stage_out writes the bf16 tile [128 queries][136] (8 pad
+// elements per row) into free LDS; store_staged then writes whole 256-byte
+// query rows, 16 lanes per row.
+constexpr int kOutRow = kHeadDim + 8;
+__device__ __forceinline__ void stage_out(uint16_t *stg, const f32x16 (&o)[4], int qloc, int lg) {
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      u32x2 v2;
+      v2[0] = pack_bf16x2(o[u][4 * jj + 0], o[u][4 * jj + 1]);
+      v2[1] = pack_bf16x2(o[u][4 * jj + 2], o[u][4 * jj + 3]);
+      st8(stg + qloc * kOutRow + 32 * u + 8 * jj + 4 * lg, v2);
+    }
+}
+template <int kThreads>
+__device__ __forceinline__ void store_staged(const uint16_t *stg, __bf16 *out0, int Hq, int tid) {
+#pragma unroll
+  for (int it = 0; it < kBlock * 16 / kThreads; ++it) {
+    const int c = it * kThreads + tid, row = c >> 4, ch = c & 15;
+    st16(out0 + (size_t)row * Hq * kHeadDim + 8 * ch, ld16(stg + row * kOutRow + 8 * ch));
+  }
 }
 
 __device__ __forceinline__ void write_empty(__bf16 *orow, float *lse, int lg) {
@@ -370,7 +402,7 @@ constexpr int kHalfV = kHeadDim * kRowVh;        // V^T half: 128 dims x 9 chunk
 constexpr uint32_t kBufWord3 = 0x00020000u;      // raw buffer descriptor word 3 (gfx9 dword access)
 
 template <bool kSparse, bool kPair>
-__global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTable t, int rows) {
+__device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTable &t, int rows, int item) {
   static_assert(kSparse || !kPair, "paired lists are block-sparse");
   __shared__ __attribute__((aligned(1024))) uint16_t K0[2 * kHalfK];   // bf16 K halves, [key][d]
   __shared__ __attribute__((aligned(1024))) uint16_t V0[2 * kHalfV];   // fp16 V^T halves, [d][key]
@@ -384,7 +416,7 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
   const int lg = lane >> 5, l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qw = wv & 3, kh = wv >> 2;
-  const AttnItem w = decode_attn(a, t, rows);
+  const AttnItem w = decode_item(a, t, rows, item);
   const int zrow = t.row[w.z];
   const size_t ztok = (size_t)t.tok[w.z];
   const size_t qtok0 = ztok + (size_t)w.I * kBlock;
@@ -702,8 +734,54 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
     for (int u = 0; u < 4; ++u)
 #pragma unroll
       for (int i = 0; i < 16; ++i) o[u][i] = (o[u][i] * a0 + xch[(16 * u + i) * 64 + lane] * a1) * inv;
-    write_out(orow, o, 1.f, lg);
+    stage_out(V0, o, qloc, lg);
     if (lse && lg == 0) *lse = kPair && !(l > 0.f) ? -INFINITY : (m + __log2f(l)) * 0.69314718055994531f;
+  }
+  block_sync();
+  store_staged<512>(V0, (__bf16 *)a.out + (qtok0 * a.Hq + w.h) * kHeadDim, a.Hq, tid);
+}
+
+// The bf16 kernel is persistent: one workgroup per CU (its LDS admits no
+// second one) loops over (head, query block) items.  Items are ordered KV
+// group, then row (longest causal prefix first), then the group's heads, and
+// cut into 8 contiguous chunks, one per XCD (workgroup b runs on XCD b % 8),
+// so an XCD's L2 serves neighbouring rows of one KV group.  Each chunk is a
+// queue (a counter in the workspace, zeroed by the V^T pre-pass): a
+// workgroup takes its XCD's next item, and once that chunk is exhausted it
+// takes items of the other chunks.  The XCDs of one part do not run at one
+// speed (up to 6 % apart on identical work), and with one item per
+// workgroup, dispatched round-robin over the XCDs, the fast ones idled for
+// up to 1.5 ms at the end of a 33 ms call; a workgroup also no longer pays a
+// dispatch per item.  The next item's counter is bumped when an item starts
+// and read when it ends, so the atomic's latency hides under the item.
+template <bool kSparse, bool kPair>
+__global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTable t, int rows, int32_t *ctr) {
+  __shared__ int32_t next_item;
+  const int n = rows * a.Hq, per = (n + 7) >> 3, xcd = blockIdx.x & 7;
+  auto lo_of = [&](int x) { return x * per; };
+  auto hi_of = [&](int x) { const int h = (x + 1) * per; return h < n ? h : n; };
+  // an item of another chunk, or -1 when every chunk is exhausted (thread 0)
+  auto steal = [&]() {
+    for (int k = 1; k < 8; ++k) {
+      const int x = (xcd + k) & 7, lo = lo_of(x), hi = hi_of(x);
+      if (lo >= hi || __hip_atomic_load(&ctr[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= hi - lo) continue;
+      const int i = atomicAdd(&ctr[x], 1);
+      if (lo + i < hi) return lo + i;
+    }
+    return -1;
+  };
+  auto own_or_steal = [&](int i) { return lo_of(xcd) + i < hi_of(xcd) ? lo_of(xcd) + i : steal(); };
+  if (threadIdx.x == 0) next_item = own_or_steal(atomicAdd(&ctr[xcd], 1));
+  __syncthreads();
+  int cur = next_item;
+  while (cur >= 0) {
+    int pending = 0;
+    if (threadIdx.x == 0) pending = atomicAdd(&ctr[xcd], 1);
+    attn_bf16_item<kSparse, kPair>(a, t, rows, cur);
+    block_sync();                    // every wave is past its last read of next_item and the item's LDS
+    if (threadIdx.x == 0) next_item = own_or_steal(pending);
+    block_sync();
+    cur = __builtin_amdgcn_readfirstlane(next_item);
   }
 }
 
@@ -967,9 +1045,14 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
 }
 
 // ================================================================ launchers
-size_t attn_workspace_bytes(int Hkv, int R, bool fp8) {
-  if (!fp8) return (size_t)Hkv * R * 2 * (size_t)kTile16;
-  return attn_workspace_scales_offset(Hkv, R) + 2 * (size_t)Hkv * R * sizeof(float);
+size_t attn_workspace_ctr_offset(int Hkv, int R, bool fp8) {
+  const size_t b = fp8 ? attn_workspace_scales_offset(Hkv, R) + 2 * (size_t)Hkv * R * sizeof(float)
+                       : (size_t)Hkv * R * 2 * (size_t)kTile16;
+  return (b + 255) / 256 * 256;
+}
+size_t attn_workspace_bytes(int Hkv, int R, bool fp8, int num_seqs) {
+  const size_t launches = (size_t)(num_seqs + kMaxSeqsPerLaunch - 1) / kMaxSeqsPerLaunch;
+  return attn_workspace_ctr_offset(Hkv, R, fp8) + (launches * 8 * sizeof(int32_t) + 255) / 256 * 256;
 }
 size_t attn_workspace_img16_offset(int Hkv, int R) { return (size_t)Hkv * R * kTile8; }
 size_t attn_workspace_scales_offset(int Hkv, int R) {
@@ -982,7 +1065,8 @@ hipError_t launch_vprep(const AttnLaunch &a, bool fp8, hipStream_t s) {
     hipLaunchKernelGGL(vprep_fp8_kernel, grid, dim3(256), 0, s, (const uint8_t *)a.v, a.vimg8, a.vimg16,
                        a.Hkv, a.R);
   else
-    hipLaunchKernelGGL(vprep_bf16_kernel, grid, dim3(256), 0, s, (const __bf16 *)a.v, a.vimg16, a.Hkv, a.R);
+    hipLaunchKernelGGL(vprep_bf16_kernel, grid, dim3(256), 0, s, (const __bf16 *)a.v, a.vimg16, a.Hkv, a.R, a.ctr,
+                       a.n_ctr);
   return hipGetLastError();
 }
 
@@ -994,8 +1078,23 @@ hipError_t launch_vprep_paged(const AttnLaunch &a, const SeqTable &t, int rows, 
   return hipGetLastError();
 }
 
+// Workgroups of the persistent bf16 kernel: one per CU of the stream's
+// device (none idle when there are fewer items).
+static int persistent_grid(hipStream_t s, int n_items) {
+  int dev = 0;
+  if (s) {
+    hipDevice_t d = 0;
+    if (hipStreamGetDevice(s, &d) == hipSuccess) dev = (int)d;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    dev = 0;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  return n_items < cus ? n_items : cus;
+}
+
 hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows, bool sparse, bool fp8, bool pv16,
-                       hipStream_t s) {
+                       int launch_index, hipStream_t s) {
   const dim3 grid(rows * a.Hq);
   if (fp8 && pv16) {
     if (sparse) hipLaunchKernelGGL((attn_fp8_kernel<true, true>), grid, dim3(256), 0, s, a, t, rows);
@@ -1004,15 +1103,17 @@ hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows, bool sp
     if (sparse) hipLaunchKernelGGL((attn_fp8_kernel<true, false>), grid, dim3(256), 0, s, a, t, rows);
     else hipLaunchKernelGGL((attn_fp8_kernel<false, false>), grid, dim3(256), 0, s, a, t, rows);
   } else {
-    if (sparse) hipLaunchKernelGGL((attn_bf16_kernel<true, false>), grid, dim3(512), 0, s, a, t, rows);
-    else hipLaunchKernelGGL((attn_bf16_kernel<false, false>), grid, dim3(512), 0, s, a, t, rows);
+    const dim3 pgrid(persistent_grid(s, rows * a.Hq));
+    int32_t *ctr = a.ctr + 8 * launch_index;
+    if (sparse) hipLaunchKernelGGL((attn_bf16_kernel<true, false>), pgrid, dim3(512), 0, s, a, t, rows, ctr);
+    else hipLaunchKernelGGL((attn_bf16_kernel<false, false>), pgrid, dim3(512), 0, s, a, t, rows, ctr);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_attn_q64(const AttnLaunch &a, const SeqTable &t, int rows, hipStream_t s) {
-  const dim3 grid(rows * a.Hq);
-  hipLaunchKernelGGL((attn_bf16_kernel<true, true>), grid, dim3(512), 0, s, a, t, rows);
+hipError_t launch_attn_q64(const AttnLaunch &a, const SeqTable &t, int rows, int launch_index, hipStream_t s) {
+  const dim3 pgrid(persistent_grid(s, rows * a.Hq));
+  hipLaunchKernelGGL((attn_bf16_kernel<true, true>), pgrid, dim3(512), 0, s, a, t, rows, a.ctr + 8 * launch_index);
   return hipGetLastError();
 }
 

@@ -290,7 +290,7 @@ size_t stem_attn_workspace_bytes(const stem_problem_t *p, int32_t dtype) {
   Shape s;
   if (check_problem(p, &s) != STEM_OK) return 0;
   if (dtype != STEM_DTYPE_BF16 && dtype != STEM_DTYPE_FP8_E4M3 && dtype != STEM_DTYPE_FP8_E4M3_PV16) return 0;
-  return attn_workspace_bytes(s.Hkv, s.R, dtype != STEM_DTYPE_BF16);
+  return attn_workspace_bytes(s.Hkv, s.R, dtype != STEM_DTYPE_BF16, s.B);
 }
 
 static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, const void *k,
@@ -318,7 +318,7 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
   }
   if (sparse && (!block_idx || !block_cnt || k_cap < 1)) return STEM_ERR_INVALID_ARG;
   if (q64 && s.max_nb > kMaxListBlocks) return STEM_ERR_UNSUPPORTED;
-  const size_t need = attn_workspace_bytes(s.Hkv, s.R, fp8);
+  const size_t need = attn_workspace_bytes(s.Hkv, s.R, fp8, s.B);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return STEM_ERR_WORKSPACE;
 
   AttnLaunch a;
@@ -358,6 +358,8 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
     a.k_scale = rs;
     a.v_scale = rs + (size_t)s.R * s.Hkv;
   }
+  a.ctr = (int32_t *)((uint8_t *)workspace + attn_workspace_ctr_offset(s.Hkv, s.R, fp8));
+  a.n_ctr = 8 * ((s.B + kMaxSeqsPerLaunch - 1) / kMaxSeqsPerLaunch);
   hipStream_t hs = as_stream(stream);
   if (!table && launch_vprep(a, fp8, hs) != hipSuccess) return STEM_ERR_HIP;
   for (int z0 = 0; z0 < s.B; z0 += kMaxSeqsPerLaunch) {
@@ -367,7 +369,9 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
     const int rows = t.row[n] - t.row[0];
     if ((int64_t)rows * s.Hq >= ((int64_t)1 << 31)) return STEM_ERR_UNSUPPORTED;
     if (table && launch_vprep_paged(a, t, rows, hs) != hipSuccess) return STEM_ERR_HIP;
-    const hipError_t e = q64 ? launch_attn_q64(a, t, rows, hs) : launch_attn(a, t, rows, sparse, fp8, pv16, hs);
+    const int li = z0 / kMaxSeqsPerLaunch;
+    const hipError_t e =
+        q64 ? launch_attn_q64(a, t, rows, li, hs) : launch_attn(a, t, rows, sparse, fp8, pv16, li, hs);
     if (e != hipSuccess) return STEM_ERR_HIP;
   }
   return STEM_OK;

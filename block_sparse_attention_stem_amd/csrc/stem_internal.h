@@ -148,19 +148,28 @@ struct AttnLaunch {
   const int32_t *table;
   int32_t table_stride, num_pages;
   const float *k_scale_pages, *v_scale_pages;
+  // Work queues of the persistent bf16 kernel: 8 counters (one per XCD) per
+  // launch, in the workspace; the V^T pre-pass zeroes n_ctr of them.
+  int32_t *ctr;
+  int32_t n_ctr;
 };
 // fp8 workspace: e4m3 V^T images, then fp16 ones, then K and V scales [R][Hkv]
 // (row-indexed copies, written by the paged pre-pass only).
-size_t attn_workspace_bytes(int Hkv, int R, bool fp8);
+// ... then the work-queue counters (8 per launch of at most kMaxSeqsPerLaunch
+// sequences), from attn_workspace_ctr_offset, 256-byte aligned.
+size_t attn_workspace_bytes(int Hkv, int R, bool fp8, int num_seqs);
+size_t attn_workspace_ctr_offset(int Hkv, int R, bool fp8);
 size_t attn_workspace_img16_offset(int Hkv, int R);
 size_t attn_workspace_scales_offset(int Hkv, int R);
 hipError_t launch_vprep(const AttnLaunch &a, bool fp8, hipStream_t s);
 // Paged pre-pass for the rows of one launch's sequences.
 hipError_t launch_vprep_paged(const AttnLaunch &a, const SeqTable &t, int rows_in_launch, hipStream_t s);
 // pv16 (fp8 only): every block's P.V with fp16 weights against the fp16 V^T image.
+// launch_index: which launch of the call this is (its 8 work-queue counters).
 hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows_in_launch,
-                       bool sparse, bool fp8, bool pv16, hipStream_t s);
+                       bool sparse, bool fp8, bool pv16, int launch_index, hipStream_t s);
 // bf16 block-sparse attention over 64-query rows (lists [Hq][2R][k_cap]).
-hipError_t launch_attn_q64(const AttnLaunch &a, const SeqTable &t, int rows_in_launch, hipStream_t s);
+hipError_t launch_attn_q64(const AttnLaunch &a, const SeqTable &t, int rows_in_launch, int launch_index,
+                           hipStream_t s);
 
 }  // namespace stem

@@ -189,7 +189,9 @@ int32_t stem_max_kept(const stem_problem_t *p, const double *k_start_host, doubl
  * with one 16-byte pad chunk per row; fp16 for bf16 inputs, e4m3 plus fp16
  * for fp8 inputs): T * Hkv * 272 bytes for bf16; for fp8, T * Hkv * 416
  * bytes plus 8 bytes per (key block, KV head) for the row-indexed K and V
- * scales that stem_bsa_prefill_paged gathers from its pages (d = 128).
+ * scales that stem_bsa_prefill_paged gathers from its pages (d = 128);
+ * rounded up to 256 bytes, then the work queues of the attention kernel:
+ * 32 bytes per launch of up to 64 sequences, rounded up to 256 bytes.
  * Contents on return are unspecified; concurrent calls need separate
  * workspaces.
  * ------------------------------------------------------------------------- */

@@ -152,8 +152,12 @@ def test_attention_argument_errors():
     assert lib.stem_bsa_prefill(p.ref, 2, f, f, f, None, None, None, f, f, 8, 0.1, f, None, f, W, None) == 1
     assert lib.stem_dense_prefill(p.ref, 2, f, f, f, f, f, f, 0.1, f, None, f, 100, None) == 4
     assert lib.stem_dense_prefill(p.ref, 3, f, f, f, f, f, f, 0.1, f, None, f, W, None) == 2
-    assert stem.stem_attn_workspace_bytes(p, 0) == 1024 * 2 * 272
-    assert stem.stem_attn_workspace_bytes(p, 1) == 1024 * 2 * 416 + (1024 // 128) * 2 * 8
+    # the V^T images (and fp8 row scales), then 256 bytes of work-queue counters
+    # (8 per launch of up to 64 sequences)
+    assert stem.stem_attn_workspace_bytes(p, 0) == 1024 * 2 * 272 + 256
+    assert stem.stem_attn_workspace_bytes(p, 1) == (1024 * 2 * 416 + (1024 // 128) * 2 * 8 + 255) // 256 * 256 + 256
+    p70 = stem.Problem([128 * i for i in range(71)], 4, 2)            # 70 sequences: two launches
+    assert stem.stem_attn_workspace_bytes(p70, 0) == 70 * 128 * 2 * 272 + 256
     assert stem.stem_attn_workspace_bytes(p, 2) == stem.stem_attn_workspace_bytes(p, 1)
     assert stem.stem_attn_workspace_bytes(p, 5) == 0
     with pytest.raises(ValueError):
