@@ -181,9 +181,12 @@ __device__ __forceinline__ void vprep_fp8_block(const uint8_t *__restrict__ v, s
 
 __global__ __launch_bounds__(256) void vprep_fp8_kernel(const uint8_t *__restrict__ v,
                                                         uint8_t *__restrict__ img8,
-                                                        uint16_t *__restrict__ img16, int Hkv, int R) {
+                                                        uint16_t *__restrict__ img16, int Hkv, int R,
+                                                        int32_t *__restrict__ ctr, int n_ctr) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kBlock * (kHeadDim + 16)];
   const int kb = blockIdx.x, g = blockIdx.y;
+  if (kb == 0 && g == 0)             // the attention kernel's work queues start empty
+    for (int i = threadIdx.x; i < n_ctr; i += 256) ctr[i] = 0;
   vprep_fp8_block(v, (size_t)kb * kBlock, kb, g, img8, img16, Hkv, R, tile);
 }
 
@@ -198,9 +201,11 @@ __global__ __launch_bounds__(256) void vprep_fp8_paged_kernel(const uint8_t *__r
                                                               int table_stride, int num_pages, SeqTable t,
                                                               const float *__restrict__ ksp,
                                                               const float *__restrict__ vsp,
-                                                              float *__restrict__ ksr, float *__restrict__ vsr) {
+                                                              float *__restrict__ ksr, float *__restrict__ vsr,
+                                                              int32_t *__restrict__ ctr) {
   __shared__ __attribute__((aligned(16))) uint8_t tile[kBlock * (kHeadDim + 16)];
   const int kb = t.row[0] + blockIdx.x, g = blockIdx.y;
+  if (blockIdx.x == 0 && g == 0 && threadIdx.x < 8) ctr[threadIdx.x] = 0;   // this launch's work queues
   const int z = seq_of(t.row, t.n, kb);
   int page = table[(size_t)(t.z0 + z) * table_stride + (kb - t.row[z])];
   page = page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
@@ -231,21 +236,6 @@ __device__ __forceinline__ AttnItem decode_item(const AttnLaunch &a, const SeqTa
   w.z = seq_of(t.row, t.n, w.r);
   w.I = w.r - t.row[w.z];
   return w;
-}
-__device__ __forceinline__ AttnItem decode_attn(const AttnLaunch &a, const SeqTable &t, int rows) {
-  return decode_item(a, t, rows, xcd_chunk_item(blockIdx.x, rows * a.Hq));
-}
-
-__device__ __forceinline__ void write_out(__bf16 *orow, const f32x16 (&o)[4], float inv, int lg) {
-#pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      u32x2 v2;
-      v2[0] = pack_bf16x2(o[u][4 * jj + 0] * inv, o[u][4 * jj + 1] * inv);
-      v2[1] = pack_bf16x2(o[u][4 * jj + 2] * inv, o[u][4 * jj + 3] * inv);
-      st8(orow + 32 * u + 8 * jj + 4 * lg, v2);
-    }
 }
 
 // The output tile goes out through LDS: in the MFMA layout a lane holds one
@@ -754,10 +744,12 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
 // up to 1.5 ms at the end of a 33 ms call; a workgroup also no longer pays a
 // dispatch per item.  The next item's counter is bumped when an item starts
 // and read when it ends, so the atomic's latency hides under the item.
-template <bool kSparse, bool kPair>
-__global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTable t, int rows, int32_t *ctr) {
+// The persistent item loop shared by the attention kernels: runs item(i)
+// for every item i in [0, n) that this workgroup claims (see above).
+template <typename F>
+__device__ __forceinline__ void run_items(int n, int32_t *ctr, F &&item) {
   __shared__ int32_t next_item;
-  const int n = rows * a.Hq, per = (n + 7) >> 3, xcd = blockIdx.x & 7;
+  const int per = (n + 7) >> 3, xcd = blockIdx.x & 7;
   auto lo_of = [&](int x) { return x * per; };
   auto hi_of = [&](int x) { const int h = (x + 1) * per; return h < n ? h : n; };
   // an item of another chunk, or -1 when every chunk is exhausted (thread 0)
@@ -777,12 +769,17 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
   while (cur >= 0) {
     int pending = 0;
     if (threadIdx.x == 0) pending = atomicAdd(&ctr[xcd], 1);
-    attn_bf16_item<kSparse, kPair>(a, t, rows, cur);
+    item(cur);
     block_sync();                    // every wave is past its last read of next_item and the item's LDS
     if (threadIdx.x == 0) next_item = own_or_steal(pending);
     block_sync();
     cur = __builtin_amdgcn_readfirstlane(next_item);
   }
+}
+
+template <bool kSparse, bool kPair>
+__global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTable t, int rows, int32_t *ctr) {
+  run_items(rows * a.Hq, ctr, [&](int i) { attn_bf16_item<kSparse, kPair>(a, t, rows, i); });
 }
 
 // ====================================================================== fp8
@@ -822,14 +819,14 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64_bs(i32x8 a, i32x8 b, f32x16 
 
 
 template <bool kSparse, bool kPV16>
-__global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable t, int rows) {
+__device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTable &t, int rows, int item) {
   __shared__ __attribute__((aligned(1024))) uint8_t Ks[kTile8];      // e4m3 K, [key][d], padded rows
   __shared__ __attribute__((aligned(1024))) uint8_t Vs[kTile8];      // e4m3 V^T image (unused with kPV16)
-  __shared__ __attribute__((aligned(1024))) uint16_t Vh[kTile16];    // fp16 V^T image (diagonal)
+  __shared__ __attribute__((aligned(1024))) uint16_t Vh[kTile16];    // fp16 V^T image (diagonal; output staging)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int lg = lane >> 5, l32 = lane & 31, sw = l32 & 7;
-  const AttnItem w = decode_attn(a, t, rows);
+  const int lg = lane >> 5, l32 = lane & 31;
+  const AttnItem w = decode_item(a, t, rows, item);
   const uint8_t *kp = (const uint8_t *)a.k;
   const int zrow = t.row[w.z];
   const size_t ztok = (size_t)t.tok[w.z];
@@ -1040,8 +1037,22 @@ __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable
   if (n_loop < n_blk) step(Diag{}, J, 0, false);
 
   const float l_tot = L + __shfl_xor(L, 32, 64);
-  write_out(orow, o, 1.f / l_tot, lg);
+  const float inv = 1.f / l_tot;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[u][i] *= inv;
+  block_sync();                      // every wave's last P.V has read Vh
+  stage_out(Vh, o, qloc, lg);
   if (lse && lg == 0) *lse = (R - kFp8Off + __log2f(l_tot)) * 0.69314718055994531f;
+  block_sync();
+  store_staged<256>(Vh, (__bf16 *)a.out + (qtok0 * a.Hq + w.h) * kHeadDim, a.Hq, tid);
+}
+
+// Persistent like the bf16 kernel (run_items), two workgroups per CU.
+template <bool kSparse, bool kPV16>
+__global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable t, int rows, int32_t *ctr) {
+  run_items(rows * a.Hq, ctr, [&](int i) { attn_fp8_item<kSparse, kPV16>(a, t, rows, i); });
 }
 
 // ================================================================ launchers
@@ -1063,24 +1074,24 @@ hipError_t launch_vprep(const AttnLaunch &a, bool fp8, hipStream_t s) {
   const dim3 grid(a.R, a.Hkv);
   if (fp8)
     hipLaunchKernelGGL(vprep_fp8_kernel, grid, dim3(256), 0, s, (const uint8_t *)a.v, a.vimg8, a.vimg16,
-                       a.Hkv, a.R);
+                       a.Hkv, a.R, a.ctr, a.n_ctr);
   else
     hipLaunchKernelGGL(vprep_bf16_kernel, grid, dim3(256), 0, s, (const __bf16 *)a.v, a.vimg16, a.Hkv, a.R, a.ctr,
                        a.n_ctr);
   return hipGetLastError();
 }
 
-hipError_t launch_vprep_paged(const AttnLaunch &a, const SeqTable &t, int rows, hipStream_t s) {
+hipError_t launch_vprep_paged(const AttnLaunch &a, const SeqTable &t, int rows, int launch_index, hipStream_t s) {
   const dim3 grid(rows, a.Hkv);
   hipLaunchKernelGGL(vprep_fp8_paged_kernel, grid, dim3(256), 0, s, (const uint8_t *)a.v, a.vimg8, a.vimg16, a.Hkv,
                      a.R, a.table, a.table_stride, a.num_pages, t, a.k_scale_pages, a.v_scale_pages,
-                     (float *)a.k_scale, (float *)a.v_scale);
+                     (float *)a.k_scale, (float *)a.v_scale, a.ctr + 8 * launch_index);
   return hipGetLastError();
 }
 
-// Workgroups of the persistent bf16 kernel: one per CU of the stream's
-// device (none idle when there are fewer items).
-static int persistent_grid(hipStream_t s, int n_items) {
+// Workgroups of a persistent attention kernel: per_cu per CU of the stream's
+// device (no more than there are items).
+static int persistent_grid(hipStream_t s, int n_items, int per_cu) {
   int dev = 0;
   if (s) {
     hipDevice_t d = 0;
@@ -1090,21 +1101,20 @@ static int persistent_grid(hipStream_t s, int n_items) {
   }
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-  return n_items < cus ? n_items : cus;
+  return n_items < cus * per_cu ? n_items : cus * per_cu;
 }
 
 hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows, bool sparse, bool fp8, bool pv16,
                        int launch_index, hipStream_t s) {
-  const dim3 grid(rows * a.Hq);
-  if (fp8 && pv16) {
-    if (sparse) hipLaunchKernelGGL((attn_fp8_kernel<true, true>), grid, dim3(256), 0, s, a, t, rows);
-    else hipLaunchKernelGGL((attn_fp8_kernel<false, true>), grid, dim3(256), 0, s, a, t, rows);
-  } else if (fp8) {
-    if (sparse) hipLaunchKernelGGL((attn_fp8_kernel<true, false>), grid, dim3(256), 0, s, a, t, rows);
-    else hipLaunchKernelGGL((attn_fp8_kernel<false, false>), grid, dim3(256), 0, s, a, t, rows);
+  int32_t *ctr = a.ctr + 8 * launch_index;
+  if (fp8) {
+    const dim3 pgrid(persistent_grid(s, rows * a.Hq, 2));
+    if (pv16 && sparse) hipLaunchKernelGGL((attn_fp8_kernel<true, true>), pgrid, dim3(256), 0, s, a, t, rows, ctr);
+    else if (pv16) hipLaunchKernelGGL((attn_fp8_kernel<false, true>), pgrid, dim3(256), 0, s, a, t, rows, ctr);
+    else if (sparse) hipLaunchKernelGGL((attn_fp8_kernel<true, false>), pgrid, dim3(256), 0, s, a, t, rows, ctr);
+    else hipLaunchKernelGGL((attn_fp8_kernel<false, false>), pgrid, dim3(256), 0, s, a, t, rows, ctr);
   } else {
-    const dim3 pgrid(persistent_grid(s, rows * a.Hq));
-    int32_t *ctr = a.ctr + 8 * launch_index;
+    const dim3 pgrid(persistent_grid(s, rows * a.Hq, 1));
     if (sparse) hipLaunchKernelGGL((attn_bf16_kernel<true, false>), pgrid, dim3(512), 0, s, a, t, rows, ctr);
     else hipLaunchKernelGGL((attn_bf16_kernel<false, false>), pgrid, dim3(512), 0, s, a, t, rows, ctr);
   }
@@ -1112,7 +1122,7 @@ hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows, bool sp
 }
 
 hipError_t launch_attn_q64(const AttnLaunch &a, const SeqTable &t, int rows, int launch_index, hipStream_t s) {
-  const dim3 pgrid(persistent_grid(s, rows * a.Hq));
+  const dim3 pgrid(persistent_grid(s, rows * a.Hq, 1));
   hipLaunchKernelGGL((attn_bf16_kernel<true, true>), pgrid, dim3(512), 0, s, a, t, rows, a.ctr + 8 * launch_index);
   return hipGetLastError();
 }

@@ -368,8 +368,8 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
     fill_table(p, z0, n, &t);
     const int rows = t.row[n] - t.row[0];
     if ((int64_t)rows * s.Hq >= ((int64_t)1 << 31)) return STEM_ERR_UNSUPPORTED;
-    if (table && launch_vprep_paged(a, t, rows, hs) != hipSuccess) return STEM_ERR_HIP;
     const int li = z0 / kMaxSeqsPerLaunch;
+    if (table && launch_vprep_paged(a, t, rows, li, hs) != hipSuccess) return STEM_ERR_HIP;
     const hipError_t e =
         q64 ? launch_attn_q64(a, t, rows, li, hs) : launch_attn(a, t, rows, sparse, fp8, pv16, li, hs);
     if (e != hipSuccess) return STEM_ERR_HIP;

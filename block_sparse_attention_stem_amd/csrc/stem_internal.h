@@ -163,7 +163,8 @@ size_t attn_workspace_img16_offset(int Hkv, int R);
 size_t attn_workspace_scales_offset(int Hkv, int R);
 hipError_t launch_vprep(const AttnLaunch &a, bool fp8, hipStream_t s);
 // Paged pre-pass for the rows of one launch's sequences.
-hipError_t launch_vprep_paged(const AttnLaunch &a, const SeqTable &t, int rows_in_launch, hipStream_t s);
+hipError_t launch_vprep_paged(const AttnLaunch &a, const SeqTable &t, int rows_in_launch, int launch_index,
+                              hipStream_t s);
 // pv16 (fp8 only): every block's P.V with fp16 weights against the fp16 V^T image.
 // launch_index: which launch of the call this is (its 8 work-queue counters).
 hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows_in_launch,
