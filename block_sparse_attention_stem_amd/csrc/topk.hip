@@ -36,22 +36,30 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                    __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Wave-wide max / min of an unsigned value (butterfly over the 64 lanes).
+// Wave-wide max / min of an unsigned value: within each row of 16 lanes by
+// DPP (pairs, quads, half-row mirror, row mirror), then across the four rows
+// through readlane; the result is uniform.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_get(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, kCtrl, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t umax2(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umin2(uint32_t a, uint32_t b) { return a < b ? a : b; }
 __device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_xor((int)x, o, 64);
-    x = x > y ? x : y;
-  }
-  return x;
+  x = umax2(x, dpp_get<0xB1>(x));
+  x = umax2(x, dpp_get<0x4E>(x));
+  x = umax2(x, dpp_get<0x141>(x));
+  x = umax2(x, dpp_get<0x140>(x));
+  return umax2(umax2((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16)),
+               umax2((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48)));
 }
 __device__ __forceinline__ uint32_t wave_umin(uint32_t x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = (uint32_t)__shfl_xor((int)x, o, 64);
-    x = x < y ? x : y;
-  }
-  return x;
+  x = umin2(x, dpp_get<0xB1>(x));
+  x = umin2(x, dpp_get<0x4E>(x));
+  x = umin2(x, dpp_get<0x141>(x));
+  x = umin2(x, dpp_get<0x140>(x));
+  return umin2(umin2((uint32_t)__builtin_amdgcn_readlane((int)x, 0), (uint32_t)__builtin_amdgcn_readlane((int)x, 16)),
+               umin2((uint32_t)__builtin_amdgcn_readlane((int)x, 32), (uint32_t)__builtin_amdgcn_readlane((int)x, 48)));
 }
 
 // One row with candidates in MC slots per lane (J = lane + 64 m, m < MC;
@@ -93,15 +101,24 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int32_t
     if (hi != lo) {
       const int top = 31 - __builtin_clz(hi ^ lo);
       T = top == 31 ? 0u : (lo & ~((2u << top) - 1u));
-      for (int bit = top; bit >= 0; --bit) {
+      // Invariant: c_T = count(key >= T) >= need.  Once c_T == need the
+      // selected set is fixed (every key >= T), so the lower bits of T are
+      // not needed; on continuous scores that happens after about
+      // log2(n_cand) bits, not all of them.
+      int c_T = n_cand;
+      for (int bit = top; bit >= 0 && c_T != need; --bit) {
         const uint32_t cand = T | (1u << bit);
         int c = 0;
 #pragma unroll
         for (int m = 0; m < MC; ++m) c += __popcll(__ballot(key[m] >= cand));
-        if (c >= need) T = cand;
+        if (c >= need) {
+          T = cand;
+          c_T = c;
+        }
       }
     }
-    // T is the need-th largest key, T >= 1: key 0 (no candidate) never counts
+    // T >= 1 and count(key >= T) >= need, with equality unless T is exactly
+    // the need-th largest key (ties): key 0 (no candidate) never counts
     int c_gt = 0;
 #pragma unroll
     for (int m = 0; m < MC; ++m) {
@@ -134,6 +151,10 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int32_t
   if (lane == 0) *ocnt = base;
 }
 
+// kMaxMC: the most slots any row of the launch needs (16 for rows of at
+// most 1024 blocks, else 32); the narrower instance needs fewer registers,
+// so more waves share each SIMD.
+template <int kMaxMC>
 __global__ __launch_bounds__(256) void topk_kernel(TopkLaunch a, SeqTable t, int rows) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int item = blockIdx.x * 4 + wave;
@@ -163,16 +184,25 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkLaunch a, SeqTable t, int
     case 2: topk_row<8>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
     case 3: topk_row<12>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
     case 4: topk_row<16>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
-    case 5: topk_row<20>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
-    case 6: topk_row<24>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
-    case 7: topk_row<28>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
-    default: topk_row<kPer>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
+    default:
+      if constexpr (kMaxMC > 16) {
+        switch ((I >> 8) + 1) {
+          case 5: topk_row<20>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
+          case 6: topk_row<24>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
+          case 7: topk_row<28>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
+          default: topk_row<kPer>(srow, orow, ocnt, a.k_cap, I, sink_end, win0, need, n_cand, lane); break;
+        }
+      }
+      break;
   }
 }
 
 hipError_t launch_topk(const TopkLaunch &a, const SeqTable &t, int rows, hipStream_t s) {
   const int waves = rows * a.Hq;
-  hipLaunchKernelGGL(topk_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, a, t, rows);
+  int max_nb = 0;
+  for (int z = 0; z < t.n; ++z) max_nb = t.row[z + 1] - t.row[z] > max_nb ? t.row[z + 1] - t.row[z] : max_nb;
+  if (max_nb <= 1024) hipLaunchKernelGGL(topk_kernel<16>, dim3((waves + 3) / 4), dim3(256), 0, s, a, t, rows);
+  else hipLaunchKernelGGL(topk_kernel<kPer>, dim3((waves + 3) / 4), dim3(256), 0, s, a, t, rows);
   return hipGetLastError();
 }
 
