@@ -160,7 +160,9 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkLaunch a, SeqTable t, int
   const int item = blockIdx.x * 4 + wave;
   if (item >= rows * a.Hq) return;
   const int h = item % a.Hq;
-  const int rl = item / a.Hq;                      // row within this launch
+  // rows in descending order: the longest rows (most slots) start first, so
+  // the short ones fill the tail of the launch
+  const int rl = rows - 1 - item / a.Hq;           // row within this launch
   const int r = t.row[0] + rl;                     // global row
   const int z = seq_of(t.row, t.n, r);
   const int I = r - t.row[z];
