@@ -61,6 +61,81 @@ def bsa_pairs(idx, cnt, p):
     return int((full * 16384 + has_diag.to(torch.int64) * 8256).sum().item())
 
 
+def q64_pairs(idx64, cnt64, p):
+    """Computed (query, key) pairs of 64-query lists (rows 2r, 2r + 1 of block
+    row r): a full block counts 64*128; the diagonal block counts 64*65/2 for
+    half 0 and 64*64 + 64*65/2 for half 1."""
+    import torch
+    rows = torch.arange(p.R, device=cnt64.device)
+    starts = torch.tensor(p.cu[:-1], device=cnt64.device) // 128
+    seq_of = torch.repeat_interleave(torch.arange(len(p.nbs), device=cnt64.device),
+                                     torch.tensor(p.nbs, device=cnt64.device))
+    I = (rows - starts[seq_of]).repeat_interleave(2)
+    half = torch.arange(2 * p.R, device=cnt64.device) % 2
+    last = torch.gather(idx64, 2, (cnt64.clamp(min=1) - 1).long().unsqueeze(-1)).squeeze(-1)
+    has_diag = ((cnt64 > 0) & (last == I.unsqueeze(0))).to(torch.int64)
+    full = cnt64.to(torch.int64) - has_diag
+    diag_pairs = torch.where(half == 0, 2080, 6176).unsqueeze(0)
+    return int((full * 8192 + has_diag * diag_pairs).sum().item())
+
+
+def union_blocks(idx_a, cnt_a, idx_b, cnt_b, max_nb):
+    """Blocks in the union of two lists per (head, row), summed."""
+    import torch
+    tot = 0
+    for h in range(idx_a.shape[0]):
+        m = torch.zeros((idx_a.shape[1], max_nb + 1), dtype=torch.bool, device=idx_a.device)
+        for ix, cn in ((idx_a[h], cnt_a[h]), (idx_b[h], cnt_b[h])):
+            valid = torch.arange(ix.shape[1], device=ix.device).unsqueeze(0) < cn.unsqueeze(1)
+            m.scatter_(1, torch.where(valid, ix.long(), max_nb), True)
+        tot += int(m[:, :max_nb].sum().item())
+    return tot
+
+
+def tile_64x128(torch, stem, p, w, qd, kd, vd, scores, idx, cnt, kcap, dout, aws, args):
+    """The paired 64 x 128 call on identical and on distinct half lists,
+    each timed alternately with the square-row call on half 0's lists."""
+    causal_blocks = p.Hq * sum(nb * (nb + 1) // 2 for nb in p.nbs)
+    dense_pairs = p.Hq * sum(L * (L + 1) / 2 for L in w.seqlens)
+    g = torch.Generator(device=scores.device)
+    g.manual_seed(64)
+    rnd = torch.rand(scores.shape, generator=g, device=scores.device, dtype=torch.float32)
+    idx_b = torch.empty_like(idx)
+    cnt_b = torch.empty_like(cnt)
+    stem.stem_schedule_topk(p, rnd, w.k_start, w.mu, w.alpha, w.n_init, w.n_window, kcap, idx_b, cnt_b)
+    del rnd
+    sq_pairs = bsa_pairs(idx, cnt, p)
+    res = {"kernel": "attn_bf16_kernel<sparse, paired 64-query lists>",
+           "square_rows_pair_fraction": sq_pairs / dense_pairs}
+    for key, (ia, ca, ib, cb) in (("same_lists", (idx, cnt, idx, cnt)), ("distinct_lists", (idx, cnt, idx_b, cnt_b))):
+        idx64 = torch.stack((ia, ib), dim=2).reshape(p.Hq, 2 * p.R, kcap).contiguous()
+        cnt64 = torch.stack((ca, cb), dim=2).reshape(p.Hq, 2 * p.R).contiguous()
+        qtimer = StageTimer(torch, ["bsa", "q64"])
+        qfn = [lambda: stem.stem_bsa_prefill(p, qd, kd, vd, idx, cnt, out=dout, workspace=aws),
+               lambda: stem.stem_bsa_prefill_q64(p, qd, kd, vd, idx64, cnt64, out=dout, workspace=aws)]
+        qtimer.run(qfn)
+        torch.cuda.synchronize()
+        qevs = [qtimer.run(qfn) for _ in range(max(3, args.steps // 2))]
+        torch.cuda.synchronize()
+        for ev in qevs:
+            qtimer.collect(ev)
+        hp = q64_pairs(idx64, cnt64, p)
+        ub = union_blocks(ia, ca, ib, cb, p.max_nb)
+        t64, tsq = qtimer.mean("q64"), qtimer.mean("bsa")
+        res[key] = {"bsa_ms": t64, "square_rows_ms_alternating": tsq,
+                    "half_pair_fraction": hp / dense_pairs,
+                    "union_block_fraction": ub / causal_blocks,
+                    "square_rows_block_fraction": int(ca.sum().item()) / causal_blocks,
+                    "ms_per_tera_pair": t64 / (hp * 1e-12),
+                    "square_rows_ms_per_tera_pair": tsq / (sq_pairs * 1e-12),
+                    "per_pair_vs_square_rows": (t64 / hp) / (tsq / sq_pairs),
+                    "tflops": 4.0 * 128 * hp / (t64 * 1e-3) / 1e12}
+        del idx64, cnt64
+    res["half_lists"] = ("distinct_lists: half 0 = the row's top-k list, half 1 = top-k of uniform random "
+                         "scores under the same schedule (seed 64)")
+    return res
+
+
 def source_sha(*names):
     """Hash of the kernel sources with comments and whitespace removed: a
     measured traffic figure stays valid across comment edits and goes stale
@@ -309,21 +384,14 @@ def run_main(args):
     for ev in evs:
         timer.collect(ev)
 
-    # the 64 x 128 variant on the same lists (each 64-query half given its
-    # row's list: same computed pairs), timed alternately with the square-row
-    # call so both see the same clock
-    idx64 = idx.repeat_interleave(2, dim=1).contiguous()
-    cnt64 = cnt.repeat_interleave(2, dim=1).contiguous()
-    qtimer = StageTimer(torch, ["bsa", "q64"])
-    qfn = [lambda: stem.stem_bsa_prefill(p, qd, kd, vd, idx, cnt, out=dout, workspace=aws),
-           lambda: stem.stem_bsa_prefill_q64(p, qd, kd, vd, idx64, cnt64, out=dout, workspace=aws)]
-    qtimer.run(qfn)
-    torch.cuda.synchronize()
-    qevs = [qtimer.run(qfn) for _ in range(max(3, args.steps // 2))]
-    torch.cuda.synchronize()
-    for ev in qevs:
-        qtimer.collect(ev)
-    del idx64, cnt64
+    # The 64 x 128 variant, timed alternately with the square-row call on
+    # (a) identical halves: each 64-query half gets its row's list (same
+    #     computed pairs as the square call);
+    # (b) distinct halves at the same budget: half 0 gets the row's list,
+    #     half 1 the top-k of uniform random scores under the same schedule,
+    #     so the two lists are nearly independent (their union is close to
+    #     the largest it can be at this budget).
+    tile64 = tile_64x128(torch, stem, p, w, qd, kd, vd, scores, idx, cnt, kcap, dout, aws, args)
     # dense on the same inputs
     dtimer = StageTimer(torch, ["dense"])
     dfn = [lambda: stem.stem_dense_prefill(p, qd, kd, vd, out=dout, workspace=aws)]
@@ -371,10 +439,7 @@ def run_main(args):
         "speedup_vs_dense": t_dense / t_stem,
         "bsa_speedup_vs_dense": t_dense / timer.mean("bsa"),
         "skip_overhead": timer.mean("bsa") / (rho * t_dense) - 1.0,
-        "tile_64x128": {"kernel": "attn_bf16_kernel<sparse, paired 64-query lists>", "bsa_ms": qtimer.mean("q64"),
-                        "square_rows_ms_alternating": qtimer.mean("bsa"),
-                        "vs_128x128": qtimer.mean("q64") / qtimer.mean("bsa"),
-                        "tflops": bsa_flop / (qtimer.mean("q64") * 1e-3) / 1e12},
+        "tile_64x128": tile64,
         "score_mfma_tflops": score_flop / (timer.mean("score") * 1e-3) / 1e12,
         "schedule_gbs": topk_bytes / (timer.mean("schedule") * 1e-3) / 1e9,
         "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<sparse>",
@@ -384,8 +449,12 @@ def run_main(args):
                      "algorithmic_flop_per_launch": bsa_flop},
     }
     log(f"[bench] stem {t_stem:.2f} ms (score {timer.mean('score'):.2f}, schedule "
-        f"{timer.mean('schedule'):.3f}, bsa {timer.mean('bsa'):.2f}); dense {t_dense:.2f} ms; "
-        f"64x128 blocks {qtimer.mean('q64'):.2f} ms vs square rows {qtimer.mean('bsa'):.2f} ms alternating")
+        f"{timer.mean('schedule'):.3f}, bsa {timer.mean('bsa'):.2f}); dense {t_dense:.2f} ms")
+    for key in ("same_lists", "distinct_lists"):
+        e = tile64[key]
+        log(f"[bench] 64x128 blocks, {key}: {e['bsa_ms']:.2f} ms for {e['half_pair_fraction']:.3f} of the pairs "
+            f"(union {e['union_block_fraction']:.3f} of the blocks); per pair {e['per_pair_vs_square_rows']:.3f}x "
+            f"the square-row call")
 
     res["reference_bf16_gemm"] = reference_gemm(torch, dev)
     log(f"[bench] reference bf16 GEMM (torch.mm, 16384^3, N(0,1) operands): "

@@ -352,10 +352,10 @@ __device__ __forceinline__ bool heavy_block(float cm, float R, float L) {
 
 // ===================================================================== bf16
 // One workgroup of 8 waves per (query head, query block), one workgroup per
-// CU.  Waves w and w + 4 share a SIMD and the same 32 queries (w & 3); wave w
-// (group 0) takes keys 0-63 of every listed block, wave w + 4 (group 1) keys
-// 64-127, each with its own online softmax, merged once per row.  A group
-// loads only its own halves of the K and V^T tiles.
+// CU.  Waves w and w + 4 share a SIMD and (square rows) the same 32 queries
+// (w & 3); wave w (group 0) takes keys 0-63 of every listed block, wave w + 4
+// (group 1) keys 64-127, each with its own online softmax, merged once per
+// row.  A group loads only its own halves of the K and V^T tiles.
 //
 // Ping-pong.  A wave alternates an MFMA phase M_b = (P.V of block b-1, then
 // S^T = K Q^T of block b) and a VALU phase X_b = (softmax of block b: mask,
@@ -377,14 +377,21 @@ __device__ __forceinline__ bool heavy_block(float cm, float R, float L) {
 // kPair: 64 x 128 blocks (64-query rows, 128-key blocks).  A workgroup still
 // runs the 128-query tile of block row r, but each 64-query half has its own
 // list (list rows 2r and 2r + 1): the tile walks the ascending union of the
-// two lists, and a block that is not in a half's list gets zero weight for
-// that half's queries.  Waves qw = 0, 1 hold half 0 and qw = 2, 3 half 1, so
-// the test is wave-uniform and such a wave skips its softmax.  The union is
-// built once per workgroup in LDS (a bitmap per half, then one wave compacts
-// their OR in ascending order), so the block loop is the square-row loop.  On gfx950
-// this costs the same per listed block as square rows (measured equal on the
-// 128K layer), whereas a 64-query tile halves the MFMA work per K/V tile but
-// keeps the tile loads and barriers (measured 2.35x slower).
+// two lists, built once per workgroup in LDS (a bitmap per half, then one
+// wave compacts their OR in ascending order).  The waves are laid out so
+// that a half can be skipped without idling a SIMD: group g holds the 64
+// queries of half g (waves 4g + {0, 1}: keys 0-63, waves 4g + {2, 3}: keys
+// 64-127), so every SIMD runs one wave of each half.  A wave skips the S^T
+// MFMAs and the softmax of a block its half does not own, and the P.V MFMAs
+// of that block one phase later; only its loads still go.  Group 0 issues
+// the loads of both key halves (group 1 reads a tile one phase after group 0
+// has waited for it), and the two groups keep the square-row ping-pong.
+// Measured on the 128K layer (~25 % of pairs per half): identical half lists
+// cost 1.10x the square-row call per computed pair, independent half lists
+// (union ~39 % of the blocks) 1.37x per computed pair; without the skip the
+// time follows the union (1.59x per pair).  A half-owned block still takes
+// two phases, in which the owning wave's MFMAs and softmax no longer overlap
+// with the other wave's, which is the remaining cost.
 constexpr float kLazyLog2 = 8.f;
 constexpr int kHalfK = 64 * kRow16;              // K half: 64 keys x 17 chunks (elements)
 constexpr int kRowVh = 72;                       // V^T half row: 64 keys + pad chunk (elements)
@@ -405,12 +412,21 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
   const int tid = threadIdx.x, lane = tid & 63;
   const int lg = lane >> 5, l32 = lane & 31;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Loader roles: wave (qw, kh) issues share qw of the tile loads of key
+  // half kh.  Compute roles: grp is the ping-pong group, cq the wave's
+  // 32-query slice and ck its key half.  Square rows: cq = qw, ck = grp = kh.
+  // kPair: group g holds the 64 queries of half g and spreads them over all
+  // four SIMDs (ck = bit 1 of the wave), so a block listed for one half only
+  // still gives every SIMD MFMA work.
   const int qw = wv & 3, kh = wv >> 2;
+  const int grp = kh;
+  const int cq = kPair ? 2 * grp + (wv & 1) : qw;
+  const int ck = kPair ? ((wv >> 1) & 1) : kh;
   const AttnItem w = decode_item(a, t, rows, item);
   const int zrow = t.row[w.z];
   const size_t ztok = (size_t)t.tok[w.z];
   const size_t qtok0 = ztok + (size_t)w.I * kBlock;
-  const int qloc = qw * 32 + l32;
+  const int qloc = cq * 32 + l32;
   const size_t qtok = qtok0 + qloc;
   // kPair: list rows 2r (queries 0-63) and 2r + 1 (queries 64-127)
   const size_t lrow = kPair ? ((size_t)w.h * a.R + w.r) * 2 : (size_t)w.h * a.R + w.r;
@@ -429,7 +445,7 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
   __bf16 *orow = (__bf16 *)a.out + (qtok * a.Hq + w.h) * kHeadDim;
   float *lse = a.lse ? a.lse + (size_t)w.h * a.T + qtok : nullptr;
   if (n_blk + n_b <= 0) {
-    if (kh == 0) write_empty(orow, lse, lg);
+    if (ck == 0) write_empty(orow, lse, lg);
     return;
   }
   auto clampJ = [&](int J) { return J < 0 ? 0 : (J > w.I ? w.I : J); };
@@ -482,7 +498,7 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
     else return kSparse ? clampJ(list[b]) : b;
   };
   auto blk = [&](int b) __attribute__((always_inline)) { return blk_entry(b) & 0xffff; };
-  const int my_bit = qw < 2 ? 1 : 2;
+  const int my_bit = grp == 0 ? 1 : 2;
 
   // Q as the B operand: query qloc, head dims 16 ks + 8 lg .. +7
   bf16x8 qf[8];
@@ -499,42 +515,51 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
   //           the pad and re-reads chunk 0).
   //   V half: 18 loads; slot s -> dim row s / 9, chunk s % 9 of this half's
   //           8 image chunks (chunk 8 is the pad and re-reads chunk 0).
+  // kPair: group 0 issues the loads of both key halves and group 1 none.
+  // Group 0 waits for its loads before the barrier that opens its MFMA phase
+  // of the block, and group 1 reads the tile one phase later, so every wave
+  // that reads a half (both groups read both) finds it landed.
+  constexpr int kLdH = kPair ? 2 : 1;              // key halves a loading wave issues
+  const bool loader = !kPair || grp == 0;
   const uint32_t kstride_b = (uint32_t)a.Hkv * kHeadDim * 2;
   const int nkk = qw == 0 ? 5 : 4, nkv = qw < 2 ? 5 : 4;
+  const int ldh = kPair ? 0 : kh;                  // first key half this wave loads
   uint32_t koff[5], voff[5];
 #pragma unroll
   for (int m = 0; m < 5; ++m) {
     const int sk = 64 * (qw + 4 * m) + lane;
-    const int rk = sk / 17, ck = sk - 17 * rk;
-    koff[m] = (uint32_t)rk * kstride_b + 16 * (ck < 16 ? ck : 0);
+    const int rk = sk / 17, chk = sk - 17 * rk;
+    koff[m] = (uint32_t)rk * kstride_b + 16 * (chk < 16 ? chk : 0);
     const int sv = 64 * (qw + 4 * m) + lane;
     const int rv = sv / 9, cv = sv - 9 * rv;
-    voff[m] = (uint32_t)(rv * kRow16 * 2 + 16 * (8 * kh + (cv < 8 ? cv : 0)));
+    voff[m] = (uint32_t)(rv * kRow16 * 2 + 16 * (8 * ldh + (cv < 8 ? cv : 0)));
   }
-  const char *kbase = (const char *)a.k + ((ztok + 64 * kh) * a.Hkv + w.g) * kHeadDim * 2;
+  const char *kbase = (const char *)a.k + ((ztok + 64 * ldh) * a.Hkv + w.g) * kHeadDim * 2;
   const char *vbase = (const char *)(a.vimg16 + ((size_t)w.g * a.R + zrow) * kTile16);
-  // Block ids are wave-uniform; readfirstlane keeps the descriptors in SGPRs.
+  // K of block J, key half ldh + hh (a descriptor of size 0 when !has:
+  // no memory is read and the buffer gets zeros).  Block ids are
+  // wave-uniform; readfirstlane keeps the descriptors in SGPRs.
+  auto k_rsrc = [&](int J, bool has, int hh) __attribute__((always_inline)) {
+    J = __builtin_amdgcn_readfirstlane(J);
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(kbase + ((size_t)J * kBlock + 64 * hh) * kstride_b), (short)0, has ? (int)(64 * kstride_b) : 0,
+        kBufWord3);
+  };
   auto issue_k = [&](int J, uint16_t *Kd) __attribute__((always_inline)) {
-    J = __builtin_amdgcn_readfirstlane(J);
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(kbase + (size_t)J * kBlock * kstride_b), (short)0, (int)(64 * kstride_b), kBufWord3);
-    uint16_t *d = Kd + kh * kHalfK;
+    if (!loader) return;
 #pragma unroll
-    for (int m = 0; m < 5; ++m)
-      if (m < nkk) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(d + (qw + 4 * m) * 512), 16, koff[m], 0, 0, 0);
+    for (int hh = 0; hh < kLdH; ++hh) {
+      const __amdgpu_buffer_rsrc_t r = k_rsrc(J, true, hh);
+      uint16_t *d = Kd + (ldh + hh) * kHalfK;
+#pragma unroll
+      for (int m = 0; m < 5; ++m)
+        if (m < nkk) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(d + (qw + 4 * m) * 512), 16, koff[m], 0, 0, 0);
+    }
   };
-  // The loads of one block step: d = 0..4 are K loads m = d of the next
-  // block (a descriptor of size 0 when there is none: no memory is read and
-  // the free buffer gets zeros), d = 5..9 are V loads m = d - 5 of this block.
-  auto k_rsrc = [&](int Jn, bool has_next) __attribute__((always_inline)) {
-    Jn = __builtin_amdgcn_readfirstlane(Jn);
-    return __builtin_amdgcn_make_buffer_rsrc((void *)(kbase + (size_t)Jn * kBlock * kstride_b), (short)0,
-                                             has_next ? (int)(64 * kstride_b) : 0, kBufWord3);
-  };
-  auto v_rsrc = [&](int J) __attribute__((always_inline)) {
+  auto v_rsrc = [&](int J, int hh) __attribute__((always_inline)) {
     J = __builtin_amdgcn_readfirstlane(J);
-    return __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + (size_t)J * kTile16 * 2), (short)0, kTile16 * 2,
-                                             kBufWord3);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(vbase + (size_t)J * kTile16 * 2 + 128 * hh), (short)0,
+                                             kTile16 * 2 - 128 * hh, kBufWord3);
   };
 
   const float c = a.scale_log2;
@@ -557,47 +582,98 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
   // operand reads issue ahead of the other wave's softmax VALU work (measured
   // 4 % on the 128K layer).
   constexpr int kAhead = 8;
-  auto mfma_phase = [&](auto kPV, const uint16_t *Vp, const uint16_t *Kc, __amdgpu_buffer_rsrc_t rk,
-                        __amdgpu_buffer_rsrc_t rv, uint16_t *Kn, uint16_t *Vc) __attribute__((always_inline)) {
+  // kPair: a wave skips the P.V MFMAs of a block its half does not own
+  // (kPV false) and the S^T MFMAs likewise (kQK false); its loads still go.
+  // The loads of one block step, d = 0 .. 10 kLdH - 1: K loads of the next
+  // block's halves (five per half), then V loads of this block's halves.
+  auto mfma_phase = [&](auto kPV, const uint16_t *Vp, const uint16_t *Kc, int J, int Jn, bool has_next,
+                        uint16_t *Kn, uint16_t *Vc, bool pv_on, bool qk_on)
+                        __attribute__((always_inline)) {
     constexpr bool PV = decltype(kPV)::value;
-    uint16_t *dk = Kn + kh * kHalfK, *dv = Vc + kh * kHalfV;
+    const __amdgpu_buffer_rsrc_t rk0 = k_rsrc(Jn, has_next, 0);
+    const __amdgpu_buffer_rsrc_t rk1 = k_rsrc(Jn, has_next, kLdH - 1);
+    // kPair: V half 1 through a descriptor 8 chunks on (an instruction offset
+    // would move the LDS destination as well)
+    const __amdgpu_buffer_rsrc_t rv = v_rsrc(J, 0);
+    const __amdgpu_buffer_rsrc_t rv1 = v_rsrc(J, kLdH - 1);
     auto dma = [&](int d) __attribute__((always_inline)) {
-      if (d < 5) {
-        if (d < nkk) __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, lds_ptr(dk + (qw + 4 * d) * 512), 16, koff[d], 0, 0, 0);
+      if (!loader) return;
+      if (d < 5 * kLdH) {
+        const int hh = d / 5, m = d % 5;
+        if (m < nkk)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(hh ? rk1 : rk0, lds_ptr(Kn + (ldh + hh) * kHalfK + (qw + 4 * m) * 512),
+                                                   16, koff[m], 0, 0, 0);
       } else {
-        const int m = d - 5;
-        if (m < nkv) __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, lds_ptr(dv + (qw + 4 * m) * 512), 16, voff[m], 0, 0, 0);
+        const int e = d - 5 * kLdH, hh = e / 5, m = e % 5;
+        if (m < nkv)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(hh ? rv1 : rv, lds_ptr(Vc + (ldh + hh) * kHalfV + (qw + 4 * m) * 512),
+                                                   16, voff[m], 0, 0, 0);
       }
     };
-    constexpr int i0 = PV ? 0 : 16;
-    const uint16_t *vad = Vp + kh * kHalfV + l32 * kRowVh + 8 * lg;
-    const uint16_t *kad = Kc + kh * kHalfK + l32 * kRow16 + 8 * lg;
+    const uint16_t *vad = Vp + ck * kHalfV + l32 * kRowVh + 8 * lg;
+    const uint16_t *kad = Kc + ck * kHalfK + l32 * kRow16 + 8 * lg;
     auto rd = [&](int i) __attribute__((always_inline)) {
       return i < 16 ? ld16(vad + 32 * kRowVh * (i & 3) + 16 * (i >> 2))
                     : ld16(kad + 32 * kRow16 * ((i - 16) & 1) + 16 * ((i - 16) >> 1));
     };
-    u32x4 r[32];
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int i = i0; i < i0 + kAhead; ++i) r[i] = rd(i);
-#pragma unroll
-    for (int i = i0; i < 32; ++i) {
-      if (i + kAhead < 32) r[i + kAhead] = rd(i + kAhead);
-      if (PV ? (i % 3 == 1 && i < 30) : (i - 16 < 10)) dma(PV ? i / 3 : i - 16);
-      __builtin_amdgcn_sched_barrier(0);
+    auto mfma = [&](int i, const u32x4 &x) __attribute__((always_inline)) {
       if (i < 16) {
-        o[i & 3] = mfma_f16_32x32x16(as_f16x8(r[i]), as_f16x8(pk[i >> 2]), o[i & 3]);
+        o[i & 3] = mfma_f16_32x32x16(as_f16x8(x), as_f16x8(pk[i >> 2]), o[i & 3]);
       } else {
         const int tt = (i - 16) & 1, ks = (i - 16) >> 1;
-        s[tt] = mfma_bf16_32x32x16(as_bf16x8(r[i]), qf[ks], ks == 0 ? f32x16{} : s[tt]);
+        s[tt] = mfma_bf16_32x32x16(as_bf16x8(x), qf[ks], ks == 0 ? f32x16{} : s[tt]);
       }
-      __builtin_amdgcn_sched_barrier(0);
+    };
+    u32x4 r[32];
+    __builtin_amdgcn_s_setprio(1);
+    if constexpr (!kPair) {
+      constexpr int i0 = PV ? 0 : 16;
+#pragma unroll
+      for (int i = i0; i < i0 + kAhead; ++i) r[i] = rd(i);
+#pragma unroll
+      for (int i = i0; i < 32; ++i) {
+        if (i + kAhead < 32) r[i + kAhead] = rd(i + kAhead);
+        if (PV ? (i % 3 == 1 && i < 30) : (i - 16 < 10)) dma(PV ? i / 3 : i - 16);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma(i, r[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      // Two parts, P.V (MFMAs 0-15, with the K loads d = 0..9) and S^T
+      // (MFMAs 16-31, with the V loads d = 10..19), each run or skipped
+      // as a whole; a skipped part still issues its loads.
+      auto part = [&](auto kPart, bool on) __attribute__((always_inline)) {
+        constexpr int p0 = 16 * decltype(kPart)::value, d0 = 10 * decltype(kPart)::value;
+        if (on) {
+#pragma unroll
+          for (int i = p0; i < p0 + kAhead; ++i) r[i] = rd(i);
+#pragma unroll
+          for (int i = p0; i < p0 + 16; ++i) {
+            if (i + kAhead < p0 + 16) r[i + kAhead] = rd(i + kAhead);
+            if (i - p0 < 10) dma(d0 + i - p0);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(i, r[i]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        } else {
+#pragma unroll
+          for (int d = d0; d < d0 + 10; ++d) dma(d);
+          // a skipped S^T is never read (its softmax is skipped too): an
+          // unspecified value keeps the old one from staying live
+          if constexpr (decltype(kPart)::value == 1) {
+            s[0] = __builtin_nondeterministic_value(s[0]);
+            s[1] = __builtin_nondeterministic_value(s[1]);
+          }
+        }
+      };
+      part(std::integral_constant<int, 0>{}, PV && pv_on);
+      part(std::integral_constant<int, 1>{}, qk_on);
     }
     __builtin_amdgcn_s_setprio(0);
   };
   // P.V of the last block (no S^T after it).
   auto pv_last = [&](const uint16_t *Vp) __attribute__((always_inline)) {
-    const uint16_t *vad = Vp + kh * kHalfV + l32 * kRowVh + 8 * lg;
+    const uint16_t *vad = Vp + ck * kHalfV + l32 * kRowVh + 8 * lg;
     u32x4 r[16];
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) r[i] = ld16(vad + 32 * kRowVh * (i & 3) + 16 * (i >> 2));
@@ -615,13 +691,13 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
   // block, keys 64-127, queries < 64): its max stays -inf, alpha stays 1 and
   // the exponent offset is 0, so every weight is 0.
   auto softmax = [&](bool diag, bool off) __attribute__((always_inline)) {
-    if (off) {                     // kPair: not in this half's list, zero weight
+    if (off) {                     // kPair: not in this half's list (its P.V is skipped too)
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) pk[cc] = u32x4{0u, 0u, 0u, 0u};
+      for (int cc = 0; cc < 4; ++cc) pk[cc] = __builtin_nondeterministic_value(pk[cc]);
       return;
     }
     if (diag) {
-      const int lim = qloc - 64 * kh - 4 * lg;        // key > qloc  <=>  local key offset > lim
+      const int lim = qloc - 64 * ck - 4 * lg;        // key > qloc  <=>  local key offset > lim
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -664,26 +740,31 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
 
   // Block b: [wait, barrier, loads for b+1, M_b, barrier, X_b].  Block b
   // uses K[b % 2] and V[b % 2]; P.V of block b-1 reads V[(b-1) % 2].
-  int own = 0;                       // kPair: ownership of the current block in bits 16-17
+  // kPair: ownership (bits 16-17) of the current block and of the previous one
+  int own = 0, own_prev = 0;
+  using NoPV = std::integral_constant<bool, false>;
+  using WithPV = std::integral_constant<bool, true>;
   auto step = [&](auto kPV, int b, int &J, const uint16_t *Kc, const uint16_t *Vp, uint16_t *Kn, uint16_t *Vc)
                   __attribute__((always_inline)) {
     const int en = b + 1 < n_blk ? blk_entry(b + 1) : 0;
     const int Jn = kPair ? (en & 0xffff) : en;
     wait_vmcnt<0>();                 // this wave's K of b and V of b-1 have landed
     block_sync();                    // ... the whole group's too; Kn and Vc are free
-    mfma_phase(kPV, Vp, Kc, k_rsrc(Jn, b + 1 < n_blk), v_rsrc(J), Kn, Vc);
+    const bool has_next = b + 1 < n_blk;
+    const bool qk_on = !kPair || ((own >> 16) & my_bit);
+    const bool pv_on = !kPair || ((own_prev >> 16) & my_bit);
+    mfma_phase(kPV, Vp, Kc, J, Jn, has_next, Kn, Vc, pv_on, qk_on);
     block_sync();
-    softmax(J == w.I, kPair && ((own >> 16) & my_bit) == 0);
+    softmax(J == w.I, !qk_on);
     J = Jn;
+    own_prev = own;
     own = en;
   };
-  using NoPV = std::integral_constant<bool, false>;
-  using WithPV = std::integral_constant<bool, true>;
 
   if constexpr (kPair) own = blk_entry(0);
   int J = blk(0);
   issue_k(J, K0);
-  if (kh == 1) block_sync();         // group 1 runs one phase behind
+  if (grp == 1) block_sync();        // group 1 runs one phase behind
   step(NoPV{}, 0, J, K0, V1, K1, V0);
   int b = 1;
   while (b < n_blk) {
@@ -695,13 +776,14 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
   // P.V of the last block, from V[(n_blk - 1) % 2]; every load has landed
   wait_vmcnt<0>();
   block_sync();
-  pv_last((n_blk & 1) ? V0 : V1);
-  if (kh == 0) block_sync();         // realign the groups
+  if (!kPair || ((own_prev >> 16) & my_bit)) pv_last((n_blk & 1) ? V0 : V1);
+  if (grp == 0) block_sync();        // realign the groups
 
-  // merge the two key halves: waves 4-7 hand (O, m, l) to waves 0-3 through LDS
+  // merge the two key halves: the key-half-1 wave of each query slice (ck = 1)
+  // hands (O, m, l) to its key-half-0 partner through LDS
   block_sync();
-  float *xch = (float *)(qw < 2 ? K0 : K1) + (qw & 1) * (66 * 64);
-  if (kh == 1) {
+  float *xch = (float *)(cq < 2 ? K0 : K1) + (cq & 1) * (66 * 64);
+  if (ck == 1) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
@@ -710,7 +792,7 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
     xch[65 * 64 + lane] = l_run;
   }
   block_sync();
-  if (kh == 0) {
+  if (ck == 0) {
     // the merged max is finite: the key equal to the query is visible in one half
     const float m1 = xch[64 * 64 + lane], l1 = xch[65 * 64 + lane];
     const float m = fmaxf(m_run, m1);

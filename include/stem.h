@@ -307,8 +307,11 @@ int stem_bsa_prefill_paged(const stem_problem_t *p, const void *q, const void *k
  *   (stem_attn_workspace_bytes(p, BF16)) likewise.  Precision as the bf16
  *   path of stem_bsa_prefill.
  * Giving both halves of a row the row's list reproduces stem_bsa_prefill
- * (bit for bit: the kernel runs the row's 128 queries over the union of the
- * two lists and gives a block zero weight in a half that does not list it).
+ * bit for bit.  The kernel walks the union of the two lists with the row's
+ * 128 queries; the waves of a half skip the MFMAs and the softmax of a block
+ * their half does not list, so the cost follows the per-half work plus a
+ * share of the union (about 1.4x the square-row call per computed pair on
+ * independent half lists at 25 %, 1.1x on identical ones).
  * Errors: as stem_bsa_prefill with dtype BF16; UNSUPPORTED for a sequence
  * longer than 4096 key blocks (512K tokens).
  * ------------------------------------------------------------------------- */
