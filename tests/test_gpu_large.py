@@ -55,6 +55,22 @@ def _gather_rows(x, rows):
     return out
 
 
+def _random_half_lists(w, idx, cnt, seed=64):
+    """Lists for the second 64-query half of every row: for the sampled heads
+    a seeded random ascending subset of [0, I] with the row's own count (so
+    the two halves of a row list mostly different blocks); for the other
+    heads the row's list."""
+    rng = np.random.default_rng(seed)
+    out = idx.copy()
+    local = np.concatenate([np.arange(L // 128) for L in w.seqlens])
+    for h in HS:
+        for r, I in enumerate(local):
+            n = int(cnt[h, r])
+            out[h, r, :n] = np.sort(rng.choice(int(I) + 1, size=n, replace=False))
+            out[h, r, n:] = -1
+    return out
+
+
 def _run(w, fp8):
     note(f"[{w.name}] generating T={w.total_tokens} Hq={w.num_q_heads} Hkv={w.num_kv_heads}")
     q, k, v = S.make_workload_qkv(w)
@@ -117,6 +133,16 @@ def _run(w, fp8):
         stem.stem_bsa_prefill_q64(p, qa, ka, va, idx.repeat_interleave(2, dim=1).contiguous(),
                                   cnt.repeat_interleave(2, dim=1).contiguous(), SCALE, out=out64, lse=lse64,
                                   workspace=aws)
+        # and with independent half lists (half 1 random, same counts): the
+        # kernel then skips, per half, the blocks that half does not list
+        idx_np, cnt_np = idx.cpu().numpy(), cnt.cpu().numpy()
+        idx_b = _random_half_lists(w, idx_np, cnt_np)
+        idx64d = np.stack((idx_np, idx_b), axis=2).reshape(p.Hq, 2 * p.R, kcap)
+        cnt64d = np.stack((cnt_np, cnt_np), axis=2).reshape(p.Hq, 2 * p.R)
+        out64d, lse64d = torch.empty_like(out), torch.empty_like(lse)
+        stem.stem_bsa_prefill_q64(p, qa, ka, va, torch.from_numpy(np.ascontiguousarray(idx64d)).to(dev()),
+                                  torch.from_numpy(np.ascontiguousarray(cnt64d)).to(dev()), SCALE, out=out64d,
+                                  lse=lse64d, workspace=aws)
     stem.stem_dense_prefill(p, qa, ka, va, SCALE, scales=scales, out=dout, workspace=aws)
     torch.cuda.synchronize()
     rows = _sample_rows(w)
@@ -136,6 +162,11 @@ def _run(w, fp8):
         res["lse64"] = {(hi, r): lse64[h, r * 128:(r + 1) * 128].to(torch.float64).cpu().numpy()
                         for hi, h in enumerate(HS) for r in rows}
         del out64, lse64
+        res["out64d"] = _gather_rows(out64d, rows)
+        res["lse64d"] = {(hi, r): lse64d[h, r * 128:(r + 1) * 128].to(torch.float64).cpu().numpy()
+                         for hi, h in enumerate(HS) for r in rows}
+        res["idx64d"], res["cnt64d"] = idx64d[HS], cnt64d[HS]
+        del out64d, lse64d
     del qd, kd, vd, out, dout, lse, scores, idx, cnt, aws, ws
     torch.cuda.empty_cache()
     bf = _subset64(q, k, v)
@@ -224,6 +255,21 @@ def test_q64_rows_on_sampled_rows(big):
                                       len(KS), SCALE, rows=pairs)
     _compare_rows(big, ro, rl, big["out64"], big["lse64"], (BF16_MAX_ABS, BF16_MEAN_REL),
                   f"{w.name} q64 {len(pairs)} rows")
+
+
+def test_q64_independent_half_lists_on_sampled_rows(big):
+    """The 64 x 128 variant with half 1 given a random list of the same count
+    (the halves then share few blocks): every sampled 64-query row against
+    the oracle with 64-query rows on the same lists."""
+    if "out64d" not in big:
+        pytest.skip("fp8 layer: the 64-query variant is bf16 only")
+    w = big["w"]
+    qs, ks, vs = big["attn_ref_inputs"]
+    pairs = [(hi, 2 * r + s) for hi in range(len(HS)) for r in big["rows"] for s in (0, 1)]
+    ro, rl = O.block_sparse_attention(qs, ks, vs, big["idx64d"], big["cnt64d"], w.cu_seqlens, len(HS), len(KS),
+                                      SCALE, rows=pairs, q_block=64)
+    _compare_rows(big, ro, rl, big["out64d"], big["lse64d"], (BF16_MAX_ABS, BF16_MEAN_REL),
+                  f"{w.name} q64 independent halves {len(pairs)} half rows")
 
 
 def test_fp8_fp16_weights_on_sampled_rows(big):
