@@ -442,6 +442,17 @@ def run_main(args):
         "tile_64x128": tile64,
         "score_mfma_tflops": score_flop / (timer.mean("score") * 1e-3) / 1e12,
         "schedule_gbs": topk_bytes / (timer.mean("schedule") * 1e-3) / 1e9,
+        # the two other stages against their own bounds (the event time of
+        # the call, launch included)
+        "stage_rooflines": {
+            "score": {"bound": "mfma", "kernel": "score_kernel", "achieved": score_flop / (timer.mean("score") * 1e-3) / 1e12,
+                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                      "frac": score_flop / (timer.mean("score") * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                      "algorithmic_flop_per_launch": score_flop},
+            "schedule": {"bound": "hbm", "kernel": "topk_kernel", "achieved": topk_bytes / (timer.mean("schedule") * 1e-3) / 1e9,
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": topk_bytes / (timer.mean("schedule") * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "algorithmic_bytes_per_launch": topk_bytes}},
         "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<sparse>",
                      "achieved": bsa_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": bsa_tflops / PEAK_BF16_TFLOPS,
