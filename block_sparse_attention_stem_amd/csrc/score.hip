@@ -162,6 +162,15 @@ hipError_t launch_vstats(const ScoreLaunch &a, const SeqTable &t, hipStream_t s)
 // permutation is applied on the global side of the loads (each lane fetches
 // the piece that belongs at its fixed LDS slot).
 //
+// The grid is persistent: one workgroup per CU walks a fixed list of tiles
+// (XCD-local, see score_item_at), and the ring runs on across tiles: the
+// last steps of a tile request the first chunks of the next one, so a tile's
+// load latency, epilogue and dispatch no longer leave the matrix core idle
+// (measured against one workgroup per tile, same box, identical scores:
+// 128K layer 7.41 against 7.59 ms, 64K 1.91 against 2.02, the fp8 varlen
+// layer 3.07 against 3.35 on bf16 and 1.55 against 2.07 on e4m3 codes).
+// The tile-independent -inf entries of S are written by score_fill_kernel.
+//
 // e4m3 inputs (kFp8): the same tile, rows and loads; a chunk is 64 codes
 // (one 64-byte piece of one token row, 16 chunks), one 32x32x64 fp8 MFMA step
 // whose 32-byte lane operand is two 16-byte pieces.  Q and K scales are
@@ -252,10 +261,64 @@ __device__ __forceinline__ void key_max_rows_and_halves(int (&k)[N]) {
   }
 }
 
+// Tile of a work item: sequence z of the launch, KV head g, query head h,
+// row band ti and column band tj <= ti, and the sequence's block count nb.
+struct ScoreTile {
+  int z, g, h, ti, tj, nb;
+};
+// Decoded without loops: the persistent kernel decodes its next tile in the
+// middle of the current one, and an inner loop there makes the register
+// allocator spill the fragments and accumulators live across it.
+__device__ __forceinline__ ScoreTile score_tile(const ScoreArgs &a, const SeqTable &t, int item) {
+  ScoreTile T;
+  const int slot = item / a.G, hh = item - slot * a.G;
+  // largest z < n with item[z] <= slot (item[] is non-decreasing, item[0] = 0
+  // <= slot): binary lifting over the kMaxSeqsPerLaunch = 64 entries
+  int z = 0;
+#pragma unroll
+  for (int step = kMaxSeqsPerLaunch / 2; step >= 1; step >>= 1) {
+    const int mid = z + step;
+    z = (mid < t.n) & (t.item[mid] <= slot) ? mid : z;
+  }
+  T.z = z;
+  const int local = slot - t.item[z];
+  T.nb = t.row[z + 1] - t.row[z];
+  const int npairs = score_pairs(T.nb);
+  T.g = local / npairs;
+  T.h = T.g * a.G + hh;
+  // row band r of pair p: r (r + 1) / 2 <= p < (r + 1) (r + 2) / 2; the fp32
+  // square-root estimate is off by at most one for p < 2^24
+  const int p = local - T.g * npairs;
+  int r = (int)((sqrtf(8.f * (float)p + 1.f) - 1.f) * 0.5f);
+  r = (r + 1) * (r + 2) / 2 <= p ? r + 1 : r;
+  r = r * (r + 1) / 2 > p ? r - 1 : r;
+  T.ti = r;
+  T.tj = p - r * (r + 1) / 2;
+  return T;
+}
+
+// The j-th item of workgroup b (-1 past its last).  A grid of one workgroup
+// per item runs item xcd_chunk_item(b) alone.  A persistent grid (a multiple
+// of 8 workgroups, fewer than the items) gives XCD x = b % 8 the contiguous
+// eighth [x per, (x + 1) per) of the items, dealt round-robin to that XCD's
+// workgroups (workgroup b takes every (grid / 8)-th item from x per + b / 8),
+// so at any time an XCD holds neighbouring tiles of one KV group in its L2;
+// the n % 8 items past the eighths go to workgroups 0 .. n % 8 - 1 last.
+__device__ __forceinline__ int score_item_at(int b, int nwg, int n_items, int j) {
+  if (nwg == n_items) return j == 0 ? xcd_chunk_item(b, n_items) : -1;
+  const int per = n_items >> 3, nx = nwg >> 3, k = b >> 3;
+  const int cnt = k < per ? (per - 1 - k) / nx + 1 : 0;
+  if (j < cnt) return (b & 7) * per + k + j * nx;
+  return (j == cnt && b < n_items - 8 * per) ? 8 * per + b : -1;
+}
+
+typedef const __attribute__((address_space(4))) float score_cfloat;   // scalar (s_load) reads
+
 template <bool kFp8>
 __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, int n_items) {
   constexpr int kEsz = kFp8 ? 1 : 2;                      // bytes per element
   constexpr int kNChunks = kFp8 ? kChunks / 2 : kChunks;  // 64 codes or 32 bf16 per chunk
+  constexpr int kStores = 16;                             // epilogue stores per wave
   __shared__ __attribute__((aligned(1024))) uint16_t A0[kTileS * kScoreBK];
   __shared__ __attribute__((aligned(1024))) uint16_t A1[kTileS * kScoreBK];
   __shared__ __attribute__((aligned(1024))) uint16_t A2[kTileS * kScoreBK];
@@ -267,30 +330,21 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int item = xcd_chunk_item(blockIdx.x, n_items);
-  const int slot = item / a.G, hh = item - slot * a.G;
-  // slot -> (sequence, KV head, tile); item prefix counts slots
-  const int z = seq_of(t.item, t.n, slot);
-  const int local = slot - t.item[z];
-  const int nb = t.row[z + 1] - t.row[z];
-  const int npairs = score_pairs(nb);
-  const int g = local / npairs;
-  const int pair = local - g * npairs;
-  const int h = g * a.G + hh;
-  int ti, tj;
-  tri_decode(pair, ti, tj);
-  const int n_rows = nb * (kBlock / 8);         // strided rows of this sequence
-  const int ibase = ti * kTileS, jbase = tj * kTileS;
-  const size_t tok0 = (size_t)t.tok[z];
+  const int wm = wave >> 1, wn = wave & 1;
+  const int b = blockIdx.x, nwg = gridDim.x;
 
   // Loads: per chunk 16 instructions for A (1024 16-byte slots) and 16 for
   // B; wave w issues A and B instructions w + 8 m (m < 2).  Slot s = 64 k +
   // lane sits at LDS row s / 4, position s % 4, and holds logical piece
   // (s % 4) ^ ((row / 4) % 4) of that row.  Rows past the sequence re-read
-  // its last row.
+  // its last row.  set_loads points the offsets and descriptors at a tile.
+  const uint32_t strideA = (uint32_t)a.Hq * kHeadDim * kEsz * 8, strideB = (uint32_t)a.Hkv * kHeadDim * kEsz * 8;
+  const uint32_t tokA = (uint32_t)a.Hq * kHeadDim * kEsz, tokB = (uint32_t)a.Hkv * kHeadDim * kEsz;
   uint32_t voffA[2], voffB[2];
-  {
-    const uint32_t strideA = (uint32_t)a.Hq * kHeadDim * kEsz * 8, strideB = (uint32_t)a.Hkv * kHeadDim * kEsz * 8;
+  __amdgpu_buffer_rsrc_t rA, rB;
+  auto set_loads = [&](const ScoreTile &T, bool live) __attribute__((always_inline)) {
+    const int n_rows = T.nb * (kBlock / 8);       // strided rows of this sequence
+    const int ibase = T.ti * kTileS, jbase = T.tj * kTileS;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int sl = 64 * (wave + 8 * m) + lane, row = sl >> 2, lc = (sl & 3) ^ ((row >> 2) & 3);
@@ -299,34 +353,35 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
       voffA[m] = (uint32_t)ra * strideA + 16 * lc;
       voffB[m] = (uint32_t)rb * strideB + 16 * lc;
     }
-  }
-  const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)((const char *)a.q + ((tok0 + 8 * (size_t)ibase) * a.Hq + h) * kHeadDim * kEsz), (short)0, 0x7fffffff,
-      kScoreBufWord3);
-  const __amdgpu_buffer_rsrc_t rB = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)((const char *)a.k + ((tok0 + 8 * (size_t)jbase) * a.Hkv + g) * kHeadDim * kEsz), (short)0, 0x7fffffff,
-      kScoreBufWord3);
-  const uint32_t tokA = (uint32_t)a.Hq * kHeadDim * kEsz, tokB = (uint32_t)a.Hkv * kHeadDim * kEsz;
+    const size_t tok0 = (size_t)t.tok[T.z];
+    rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const char *)a.q + ((tok0 + 8 * (size_t)ibase) * a.Hq + T.h) * kHeadDim * kEsz), (short)0,
+        live ? 0x7fffffff : 0, kScoreBufWord3);
+    rB = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const char *)a.k + ((tok0 + 8 * (size_t)jbase) * a.Hkv + T.g) * kHeadDim * kEsz), (short)0,
+        live ? 0x7fffffff : 0, kScoreBufWord3);
+  };
   // chunk c: token t = c / 4 of the stride group (reversed for K), dims 32 (c % 4);
   // kFp8: token t = c / 2, codes 64 (c % 2)
+  // wl, tA and tB are wave, tokA and tokB, re-declared opaque at the top of
+  // every tile (an empty asm): otherwise the compiler hoists each chunk's
+  // LDS destinations and scalar offsets, loop-invariant, out of the tile
+  // loop, and holding those ~80 values across it overflows the SGPRs.
+  int wl = wave;
+  uint32_t tA = tokA, tB = tokB;
   auto issue = [&](int c, uint16_t *Ad, uint16_t *Bd) __attribute__((always_inline)) {
     const int tt = kFp8 ? c >> 1 : c >> 2, d2 = (kFp8 ? (c & 1) : (c & 3)) * 64;
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void_t *)(Ad + (wave + 8 * m) * 512), 16, voffA[m],
-                                               (int)(tt * tokA + d2), 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void_t *)(Bd + (wave + 8 * m) * 512), 16, voffB[m],
-                                               (int)((7 - tt) * tokB + d2), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void_t *)(Ad + (wl + 8 * m) * 512), 16, voffA[m],
+                                               (int)(tt * tA + d2), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void_t *)(Bd + (wl + 8 * m) * 512), 16, voffB[m],
+                                               (int)((7 - tt) * tB + d2), 0, 0);
     }
   };
 
   f32x16 acc[2][4];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = f32x16{};
 
-  const int wm = wave >> 1, wn = wave & 1;
   const int frow = lane & 31, lg = lane >> 5;
   // fragment rows wm*64 + 32 mi + frow (A) and wn*128 + 32 nj + frow (B):
   // the permutation key (row / 4) % 4 is (frow / 4) % 4 for all of them
@@ -393,132 +448,248 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
     else read_frags(f, A3, B3);
   };
 
-  // Step c: wait for chunk c+1, barrier (chunk c's fragments, read in step
-  // c-1, are out of its stage everywhere), then run chunk c's MFMAs from
-  // registers with the loads of chunk c+4 into that stage and the fragment
-  // reads of chunk c+1 issued between them.
-  Frags fr[2];
-  score_static_for<kStages>([&](auto C_) {
-    stage_issue(std::integral_constant<int, decltype(C_)::value>{}, decltype(C_)::value);
-  });
-  score_wait_vmcnt<4 * (kStages - 1)>();
-  score_sync();
-  stage_read(std::integral_constant<int, 0>{}, fr[0]);
-  score_static_for<kNChunks>([&](auto C_) {
-    constexpr int c = decltype(C_)::value;
-    if constexpr (c + 1 < kNChunks) {
-      // loads of chunks c+2 .. c+3 (4 per wave each) may still fly
-      constexpr int later = (kNChunks - 2 - c < kStages - 2 ? kNChunks - 2 - c : kStages - 2) * 4;
-      score_wait_vmcnt<later>();
-      score_sync();
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (c + kStages < kNChunks)
-        stage_issue(std::integral_constant<int, c % kStages>{}, c + kStages);
-      stage_read(std::integral_constant<int, (c + 1) % kStages>{}, fr[(c + 1) & 1]);
-      mfmas(fr[c & 1]);
-      // The loads and fragment reads go between the MFMAs (none depends on
-      // them): per group of four MFMAs, one fragment read after each of the
-      // first three and one tile load after the first.  Issued as a burst
-      // before the MFMAs they held both waves of a SIMD off the matrix core
-      // at the start of every step.
-      if constexpr (kFp8) {
-        // 8 MFMAs, 12 fragment reads, 4 loads: per pair of MFMAs, three reads and a load
-        score_static_for<4>([&](auto) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        });
-      } else {
-        score_static_for<4>([&](auto) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
-          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        });
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    } else {
-      __builtin_amdgcn_sched_barrier(0);
-      mfmas(fr[c & 1]);
-      __builtin_amdgcn_sched_barrier(0);
+  // Epilogue operands, read through scalar loads during the tile (their
+  // wait is the lgkmcnt(0) of a later barrier): this wave's block columns
+  // J = 16 tj + 8 wn + e (e < 8) and rows I = 16 ti + 4 wm + e (e < 4),
+  // clamped into the sequence (values of clamped entries are never stored).
+  float bon_s[8], ksc_s[8], qsc_s[4];
+  auto load_epilogue = [&](const ScoreTile &T) __attribute__((always_inline)) {
+    const int r0 = t.row[T.z], j0 = 16 * T.tj + 8 * wn, i0 = 16 * T.ti + 4 * wm;
+    score_cfloat *bon = (score_cfloat *)a.bonus + (size_t)T.g * a.R + r0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int J = j0 + e < T.nb ? j0 + e : T.nb - 1;
+      bon_s[e] = bon[J];
+      if constexpr (kFp8) ksc_s[e] = ((score_cfloat *)a.k_scale)[(size_t)(r0 + J) * a.Hkv + T.g];
     }
-  });
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int I = i0 + e < T.nb ? i0 + e : T.nb - 1;
+        qsc_s[e] = ((score_cfloat *)a.q_scale)[(size_t)(r0 + I) * a.Hq + T.h];
+      }
+    }
+  };
 
-  // ---- epilogue: causal mask, 16x16 max-pool, scale, bonus
-  const bool diag = (ti == tj);
-  const size_t srow0 = ((size_t)h * a.R + t.row[z]) * a.max_nb;
-  const float *bon = a.bonus + (size_t)g * a.R + t.row[z];
-  if (diag) {
-    // the strided causal mask j <= i (only the diagonal tile crosses it)
+  // Causal mask, 16x16 max-pool, scale and bonus; then exactly kStores
+  // buffer stores per wave into the tile's row band of S, whatever the
+  // tile: a lane with nothing to store (or a block past the sequence) gives
+  // an offset beyond the descriptor's range, which drops its store.  The
+  // fixed count keeps the vmcnt arithmetic of the next tile's waits exact.
+  auto epilogue = [&](const ScoreTile &T) __attribute__((always_inline)) {
+    if (T.ti == T.tj) {
+      // The strided causal mask j <= i (only the diagonal tile crosses it).
+      // There ibase = jbase, and MFMA tile (mi, nj) of this wave starts
+      // off = 128 wn + 32 nj - 64 wm - 32 mi columns right of its first
+      // row (a multiple of 32, the same for the whole wave): off > 0 is
+      // wholly above the diagonal, off < 0 wholly below, and off = 0 holds
+      // it, with j - i = d - (8 (r / 4) + r % 4) for element r of the lane.
+      // d is made opaque so that the compiler does not hoist its
+      // loop-invariant compares out of the tile loop.
+      int d = (lane & 31) - 4 * (lane >> 5);
+      asm volatile("" : "+v"(d));
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < 4; ++nj) {
+          const int off = 128 * wn + 32 * nj - 64 * wm - 32 * mi;
+          if (off > 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[mi][nj][r] = -INFINITY;
+          } else if (off == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (d > 8 * (r >> 2) + (r & 3)) acc[mi][nj][r] = -INFINITY;
+          }
+        }
+    }
+    // per lane: the max of its 8 rows of each 16-row half, then across lanes
+    int key[16];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
       for (int nj = 0; nj < 4; ++nj) {
-        const int ib = ibase + wm * 64 + mi * 32, j = jbase + wn * 128 + nj * 32 + (lane & 31);
+        float m0 = acc[mi][nj][0], m1 = acc[mi][nj][8];
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (j > ib + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) acc[mi][nj][r] = -INFINITY;
-      }
-  }
-  // per lane: the max of its 8 rows of each 16-row half, then across lanes
-  int key[16];
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int nj = 0; nj < 4; ++nj) {
-      float m0 = acc[mi][nj][0], m1 = acc[mi][nj][8];
-#pragma unroll
-      for (int r = 1; r < 8; ++r) {
-        m0 = fmaxf(m0, acc[mi][nj][r]);
-        m1 = fmaxf(m1, acc[mi][nj][8 + r]);
-      }
-      key[8 * mi + 2 * nj] = max_key(m0);
-      key[8 * mi + 2 * nj + 1] = max_key(m1);
-    }
-  key_max_rows_and_halves(key);
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
-#pragma unroll
-    for (int nj = 0; nj < 4; ++nj) {
-      const int ib = ibase + wm * 64 + mi * 32;    // strided row base
-      const int jb = jbase + wn * 128 + nj * 32;
-      if ((lane & 15) == 0 && lane < 32) {
-        const float m0 = key_max(key[8 * mi + 2 * nj]), m1 = key_max(key[8 * mi + 2 * nj + 1]);
-        const int J = jb / 16 + (lane >> 4);
-        const int I0 = ib / 16;
-        if (J < nb) {
-          if constexpr (kFp8) {
-            // scores of the dequantised values: raw max x q scale of row I x k scale of J
-            const size_t r0 = (size_t)t.row[z];
-            const float sk = a.scale * a.k_scale[(r0 + J) * a.Hkv + g];
-            if (I0 < nb) a.scores[srow0 + (size_t)I0 * a.max_nb + J] = m0 * (sk * a.q_scale[(r0 + I0) * a.Hq + h]) + bon[J];
-            if (I0 + 1 < nb)
-              a.scores[srow0 + (size_t)(I0 + 1) * a.max_nb + J] = m1 * (sk * a.q_scale[(r0 + I0 + 1) * a.Hq + h]) + bon[J];
-          } else {
-            if (I0 < nb) a.scores[srow0 + (size_t)I0 * a.max_nb + J] = m0 * a.scale + bon[J];
-            if (I0 + 1 < nb) a.scores[srow0 + (size_t)(I0 + 1) * a.max_nb + J] = m1 * a.scale + bon[J];
-          }
+        for (int r = 1; r < 8; ++r) {
+          m0 = fmaxf(m0, acc[mi][nj][r]);
+          m1 = fmaxf(m1, acc[mi][nj][8 + r]);
         }
+        key[8 * mi + 2 * nj] = max_key(m0);
+        key[8 * mi + 2 * nj + 1] = max_key(m1);
+      }
+    key_max_rows_and_halves(key);
+    const int rows = T.nb - 16 * T.ti < 16 ? T.nb - 16 * T.ti : 16;
+    const __amdgpu_buffer_rsrc_t rS = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(a.scores + ((size_t)T.h * a.R + t.row[T.z] + 16 * T.ti) * a.max_nb), (short)0,
+        rows * a.max_nb * 4, kScoreBufWord3);
+    const int hl = (lane >> 4) & 1;
+    const bool writer = (lane & 15) == 0 && lane < 32;
+    __builtin_amdgcn_sched_barrier(0);    // the stores stay between this tile's loads and the next tile's
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+      for (int nj = 0; nj < 4; ++nj) {
+        const int Jl = 16 * T.tj + 8 * wn + 2 * nj + hl;   // block column in the sequence
+        const int Il = 4 * wm + 2 * mi;                      // block row within the band
+        const float m0 = key_max(key[8 * mi + 2 * nj]), m1 = key_max(key[8 * mi + 2 * nj + 1]);
+        const float bn = hl ? bon_s[2 * nj + 1] : bon_s[2 * nj];
+        float v0, v1;
+        if constexpr (kFp8) {
+          // scores of the dequantised values: raw max x q scale of row I x k scale of J
+          const float sk = a.scale * (hl ? ksc_s[2 * nj + 1] : ksc_s[2 * nj]);
+          v0 = m0 * (sk * qsc_s[2 * mi]) + bn;
+          v1 = m1 * (sk * qsc_s[2 * mi + 1]) + bn;
+        } else {
+          v0 = m0 * a.scale + bn;
+          v1 = m1 * a.scale + bn;
+        }
+        const bool ok = writer && Jl < T.nb;
+        const uint32_t o0 = ok ? (uint32_t)(Il * a.max_nb + Jl) * 4u : 0x80000000u;
+        const uint32_t o1 = ok ? (uint32_t)((Il + 1) * a.max_nb + Jl) * 4u : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v0), rS, (int)o0, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v1), rS, (int)o1, 0, 0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Pipeline.  Step c of a tile: wait for chunk c+1, barrier (chunk c's
+  // fragments, read in step c-1, are out of its stage everywhere), issue the
+  // loads of chunk c+4 into that stage, then run chunk c's MFMAs from
+  // registers with the fragment reads of chunk c+1 between them.  The grid
+  // is persistent: in the last steps of a tile the chunks "c+4" are chunks
+  // 0-2 of the workgroup's next tile, so its loads fly during the end of
+  // this tile and its epilogue; chunk 3 follows at the next tile's first
+  // barrier.  In-flight loads per wave at each wait (4 per chunk, in issue
+  // order with the 16 epilogue stores): the chunks after the awaited one,
+  // plus the stores while they sit behind it (the first tile is preceded by
+  // 16 stores to an empty range, so every tile sees the same sequence).
+  const int first = score_item_at(b, nwg, n_items, 0);
+  if (first < 0) return;
+  ScoreTile T = score_tile(a, t, first);
+  set_loads(T, true);
+  stage_issue(std::integral_constant<int, 0>{}, 0);
+  stage_issue(std::integral_constant<int, 1>{}, 1);
+  stage_issue(std::integral_constant<int, 2>{}, 2);
+  {
+    const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(a.scores, (short)0, 0, kScoreBufWord3);
+    __builtin_amdgcn_sched_barrier(0);    // the counts need the loads before the stores
+#pragma unroll
+    for (int i = 0; i < kStores; ++i)   // offsets 4 KB apart: never merged into wider stores
+      __builtin_amdgcn_raw_buffer_store_b32(0u, none, 4096 * i, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
-  if (diag) {
-    // -inf for the columns this row band never computes: J beyond the tile
-    // (non-causal) and J >= nb (past the sequence, up to max_nb).
-    int jstart = (ti + 1) * 16;
-    if (jstart > nb) jstart = nb;
-    const int width = a.max_nb - jstart;
-    for (int e = tid; e < 16 * width; e += 512) {
-      const int I = ti * 16 + e / width, J = jstart + e % width;
-      if (I < nb) a.scores[srow0 + (size_t)I * a.max_nb + J] = -INFINITY;
+  Frags fr[2];
+  int j = 0;
+  while (true) {
+    // the next tile is decoded here, where no accumulator or fragment is
+    // live (decoded mid-tile, its temporaries pushed the fp8 kernel past
+    // 256 VGPRs)
+    const int nxt = score_item_at(b, nwg, n_items, j + 1);
+    const bool has_next = nxt >= 0;
+    const ScoreTile Tn = has_next ? score_tile(a, t, nxt) : T;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < 4; ++nj) acc[mi][nj] = f32x16{};
+    asm volatile("" : "+s"(wl), "+s"(tA), "+s"(tB));
+    score_wait_vmcnt<8 + kStores>();              // chunk 0 (chunks 1, 2 and the stores may fly)
+    score_sync();
+    stage_issue(std::integral_constant<int, 3>{}, 3);
+    stage_read(std::integral_constant<int, 0>{}, fr[0]);
+    score_static_for<kNChunks>([&](auto C_) {
+      constexpr int c = decltype(C_)::value;
+      if constexpr (c + 1 < kNChunks) {
+        if constexpr (c < 2) score_wait_vmcnt<8 + kStores>();   // the stores sit behind chunk c+1
+        else score_wait_vmcnt<8>();
+        score_sync();
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (c + kStages < kNChunks) {
+          stage_issue(std::integral_constant<int, c % kStages>{}, c + kStages);
+          if constexpr (c + kStages + 1 == kNChunks) {
+            // this tile's last load is out: point the loads at the next tile
+            // (after the last tile, at an empty range: the loads still go,
+            // read nothing and fill stages that are not read again, so the
+            // counts above hold for every tile)
+            set_loads(Tn, has_next);
+          }
+        } else {
+          stage_issue(std::integral_constant<int, c % kStages>{}, c + kStages - kNChunks);
+        }
+        if constexpr (c == 4) load_epilogue(T);
+        stage_read(std::integral_constant<int, (c + 1) % kStages>{}, fr[(c + 1) & 1]);
+        mfmas(fr[c & 1]);
+        // The loads and fragment reads go between the MFMAs (none depends on
+        // them): per group of four MFMAs, one fragment read after each of the
+        // first three and one tile load after the first.  Issued as a burst
+        // before the MFMAs they held both waves of a SIMD off the matrix core
+        // at the start of every step.
+        if constexpr (kFp8) {
+          // 8 MFMAs, 12 fragment reads, 4 loads: per pair of MFMAs, three reads and a load
+          score_static_for<4>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          });
+        } else {
+          score_static_for<4>([&](auto) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // buffer load
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          });
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(fr[c & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+    epilogue(T);
+    if (!has_next) {
+      score_wait_vmcnt<0>();       // no load into the LDS may outlive the workgroup
+      break;
     }
+    T = Tn;
+    ++j;
   }
+}
+
+// Entries of S no tile writes: for block row I of a sequence with nb blocks,
+// J in [min(nb, 16 (I / 16 + 1)), max_nb), i.e. past the row's diagonal tile
+// (non-causal) or past the sequence; they are -inf.  One workgroup per
+// (block row, query head) of the launch.
+__global__ __launch_bounds__(256) void score_fill_kernel(float *__restrict__ scores, SeqTable t, int R,
+                                                         int max_nb) {
+  const int r = t.row[0] + blockIdx.x, h = blockIdx.y;
+  const int z = seq_of(t.row, t.n, r);
+  const int I = r - t.row[z], nb = t.row[z + 1] - t.row[z];
+  int j0 = 16 * (I / 16 + 1);
+  if (j0 > nb) j0 = nb;
+  float *row = scores + ((size_t)h * R + r) * max_nb;
+  for (int J = j0 + (int)threadIdx.x; J < max_nb; J += 256) row[J] = -INFINITY;
+}
+
+// CUs of the stream's device (256 if the query fails).
+static int score_device_cus(hipStream_t s) {
+  int dev = 0;
+  if (s) {
+    hipDevice_t d = 0;
+    if (hipStreamGetDevice(s, &d) == hipSuccess) dev = (int)d;
+  } else if (hipGetDevice(&dev) != hipSuccess) {
+    dev = 0;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  return cus;
 }
 
 hipError_t launch_score(const ScoreLaunch &l, const SeqTable &t, int n_items, hipStream_t s) {
@@ -535,8 +706,18 @@ hipError_t launch_score(const ScoreLaunch &l, const SeqTable &t, int n_items, hi
   a.max_nb = l.max_nb;
   a.G = l.Hq / l.Hkv;
   a.scale = l.scale;
-  if (l.fp8) hipLaunchKernelGGL(score_kernel<true>, dim3(n_items), dim3(512), 0, s, a, t, n_items);
-  else hipLaunchKernelGGL(score_kernel<false>, dim3(n_items), dim3(512), 0, s, a, t, n_items);
+  const int rows = t.row[t.n] - t.row[0];
+  hipLaunchKernelGGL(score_fill_kernel, dim3(rows, l.Hq), dim3(256), 0, s, l.scores, t, l.R, l.max_nb);
+  // persistent: one workgroup per CU (a multiple of 8), or one per item when
+  // there are no more items than that
+  const int cus = score_device_cus(s);
+  int grid = n_items < cus ? n_items : cus;
+  if (grid < n_items) {
+    grid &= ~7;
+    if (grid < 8) grid = n_items < 8 ? n_items : 8;
+  }
+  if (l.fp8) hipLaunchKernelGGL(score_kernel<true>, dim3(grid), dim3(512), 0, s, a, t, n_items);
+  else hipLaunchKernelGGL(score_kernel<false>, dim3(grid), dim3(512), 0, s, a, t, n_items);
   return hipGetLastError();
 }
 
