@@ -206,7 +206,7 @@ def stem_score(p: Problem, q, k, v, stride: int = 8, chunk_size: int = 2048, nor
     return scores
 
 
-STEM_SCORE_SCRATCH_BYTES = 1 << 20      # the library's own scratch per GPU (stem_score_noalloc)
+STEM_SCORE_SCRATCH_BYTES = (1 << 20) + 4096   # the library's own scratch per GPU (stem_score_noalloc)
 
 
 def stem_score_noalloc(p: Problem, q, k, v, scores: torch.Tensor, stride: int = 8, chunk_size: int = 2048,

@@ -24,10 +24,15 @@ namespace stem {
 // ------------------------------------------------------------------ vnorm
 // One workgroup per (global key block, KV head); 16 lanes per token row
 // (16 x 16 B = 256 B = one head vector), 16 rows per pass.
+// Both value-norm kernels also zero the scoring kernel's work-queue counters
+// (ctr, n_ctr of them), which run after them on the same stream.
 __global__ __launch_bounds__(256) void vnorm_kernel(const __bf16 *__restrict__ v,
-                                                    float *__restrict__ ell, int Hkv, int R) {
+                                                    float *__restrict__ ell, int Hkv, int R,
+                                                    int32_t *__restrict__ ctr, int n_ctr) {
   const int kb = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, sub = tid & 15, rowg = tid >> 4;
+  if (kb == 0 && g == 0)
+    for (int i = tid; i < n_ctr; i += 256) ctr[i] = 0;
   __shared__ float red[16];
   float emax = 0.f;
   for (int t = rowg; t < kBlock; t += 16) {
@@ -58,9 +63,12 @@ __global__ __launch_bounds__(256) void vnorm_kernel(const __bf16 *__restrict__ v
 // e4m3 V: ||V_t||^2 = vs_J^2 sum_d code_d^2 with vs_J the block's V scale.
 // 8 lanes per token row (8 x 16 codes), 32 rows per pass.
 __global__ __launch_bounds__(256) void vnorm_fp8_kernel(const uint8_t *__restrict__ v, const float *__restrict__ vsc,
-                                                        float *__restrict__ ell, int Hkv, int R) {
+                                                        float *__restrict__ ell, int Hkv, int R,
+                                                        int32_t *__restrict__ ctr, int n_ctr) {
   const int kb = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x, sub = tid & 7, rowg = tid >> 3;
+  if (kb == 0 && g == 0)
+    for (int i = tid; i < n_ctr; i += 256) ctr[i] = 0;
   __shared__ float red[32];
   float emax = 0.f;
   for (int t = rowg; t < kBlock; t += 32) {
@@ -94,9 +102,10 @@ __global__ __launch_bounds__(256) void vnorm_fp8_kernel(const uint8_t *__restric
 hipError_t launch_vnorm(const ScoreLaunch &a, hipStream_t s) {
   dim3 grid(a.R, a.Hkv);
   if (a.fp8)
-    hipLaunchKernelGGL(vnorm_fp8_kernel, grid, dim3(256), 0, s, (const uint8_t *)a.v, a.v_scale, a.ell, a.Hkv, a.R);
+    hipLaunchKernelGGL(vnorm_fp8_kernel, grid, dim3(256), 0, s, (const uint8_t *)a.v, a.v_scale, a.ell, a.Hkv, a.R,
+                       a.ctr, a.n_ctr);
   else
-    hipLaunchKernelGGL(vnorm_kernel, grid, dim3(256), 0, s, (const __bf16 *)a.v, a.ell, a.Hkv, a.R);
+    hipLaunchKernelGGL(vnorm_kernel, grid, dim3(256), 0, s, (const __bf16 *)a.v, a.ell, a.Hkv, a.R, a.ctr, a.n_ctr);
   return hipGetLastError();
 }
 
@@ -297,25 +306,10 @@ __device__ __forceinline__ ScoreTile score_tile(const ScoreArgs &a, const SeqTab
   return T;
 }
 
-// The j-th item of workgroup b (-1 past its last).  A grid of one workgroup
-// per item runs item xcd_chunk_item(b) alone.  A persistent grid (a multiple
-// of 8 workgroups, fewer than the items) gives XCD x = b % 8 the contiguous
-// eighth [x per, (x + 1) per) of the items, dealt round-robin to that XCD's
-// workgroups (workgroup b takes every (grid / 8)-th item from x per + b / 8),
-// so at any time an XCD holds neighbouring tiles of one KV group in its L2;
-// the n % 8 items past the eighths go to workgroups 0 .. n % 8 - 1 last.
-__device__ __forceinline__ int score_item_at(int b, int nwg, int n_items, int j) {
-  if (nwg == n_items) return j == 0 ? xcd_chunk_item(b, n_items) : -1;
-  const int per = n_items >> 3, nx = nwg >> 3, k = b >> 3;
-  const int cnt = k < per ? (per - 1 - k) / nx + 1 : 0;
-  if (j < cnt) return (b & 7) * per + k + j * nx;
-  return (j == cnt && b < n_items - 8 * per) ? 8 * per + b : -1;
-}
-
 typedef const __attribute__((address_space(4))) float score_cfloat;   // scalar (s_load) reads
 
 template <bool kFp8>
-__global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, int n_items) {
+__global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, int n_items, int32_t *ctr) {
   constexpr int kEsz = kFp8 ? 1 : 2;                      // bytes per element
   constexpr int kNChunks = kFp8 ? kChunks / 2 : kChunks;  // 64 codes or 32 bf16 per chunk
   constexpr int kStores = 16;                             // epilogue stores per wave
@@ -331,7 +325,6 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int b = blockIdx.x, nwg = gridDim.x;
 
   // Loads: per chunk 16 instructions for A (1024 16-byte slots) and 16 for
   // B; wave w issues A and B instructions w + 8 m (m < 2).  Slot s = 64 k +
@@ -484,10 +477,12 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
       // row (a multiple of 32, the same for the whole wave): off > 0 is
       // wholly above the diagonal, off < 0 wholly below, and off = 0 holds
       // it, with j - i = d - (8 (r / 4) + r % 4) for element r of the lane.
-      // d is made opaque so that the compiler does not hoist its
-      // loop-invariant compares out of the tile loop.
-      int d = (lane & 31) - 4 * (lane >> 5);
-      asm volatile("" : "+v"(d));
+      // d is formed from an opaque copy of the lane index, so that the
+      // compiler neither hoists its loop-invariant compares out of the tile
+      // loop nor keeps d itself live (spilled) across it.
+      int ln = lane;
+      asm volatile("" : "+v"(ln));
+      const int d = (ln & 31) - 4 * (ln >> 5);
 #pragma unroll
       for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
@@ -525,6 +520,13 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
         rows * a.max_nb * 4, kScoreBufWord3);
     const int hl = (lane >> 4) & 1;
     const bool writer = (lane & 15) == 0 && lane < 32;
+    // x1 for lanes 16-31, x0 for the others, as a bit select: written as
+    // hl ? x[1] : x[0] the compiler turns it into x[hl], an indexed read
+    // of a scratch copy of the array
+    const uint32_t hmask = 0u - (uint32_t)hl;
+    auto pick = [&](float x0, float x1) __attribute__((always_inline)) {
+      return __uint_as_float((__float_as_uint(x1) & hmask) | (__float_as_uint(x0) & ~hmask));
+    };
     __builtin_amdgcn_sched_barrier(0);    // the stores stay between this tile's loads and the next tile's
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
@@ -533,11 +535,11 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
         const int Jl = 16 * T.tj + 8 * wn + 2 * nj + hl;   // block column in the sequence
         const int Il = 4 * wm + 2 * mi;                      // block row within the band
         const float m0 = key_max(key[8 * mi + 2 * nj]), m1 = key_max(key[8 * mi + 2 * nj + 1]);
-        const float bn = hl ? bon_s[2 * nj + 1] : bon_s[2 * nj];
+        const float bn = pick(bon_s[2 * nj], bon_s[2 * nj + 1]);
         float v0, v1;
         if constexpr (kFp8) {
           // scores of the dequantised values: raw max x q scale of row I x k scale of J
-          const float sk = a.scale * (hl ? ksc_s[2 * nj + 1] : ksc_s[2 * nj]);
+          const float sk = a.scale * pick(ksc_s[2 * nj], ksc_s[2 * nj + 1]);
           v0 = m0 * (sk * qsc_s[2 * mi]) + bn;
           v1 = m1 * (sk * qsc_s[2 * mi + 1]) + bn;
         } else {
@@ -565,7 +567,36 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
   // order with the 16 epilogue stores): the chunks after the awaited one,
   // plus the stores while they sit behind it (the first tile is preceded by
   // 16 stores to an empty range, so every tile sees the same sequence).
-  const int first = score_item_at(b, nwg, n_items, 0);
+  // Work queue (as for the attention kernels): XCD x = blockIdx % 8 owns
+  // the contiguous items [x per, (x + 1) per), handed out in order by the
+  // counter ctr[x] (zeroed by the value-norm kernel), so an XCD's
+  // workgroups hold neighbouring tiles of one KV group in its L2 at any
+  // time; once its items are gone a workgroup takes items of the other
+  // XCDs.  Thread 0 claims one tile ahead of the decode: at the top of tile
+  // n it turns the counter value fetched at tile n-1 into the item of tile
+  // n+2 (an LDS slot by parity) and fetches the next value, so no atomic
+  // result is waited for inside the tile.
+  __shared__ int32_t q_slot[3];
+  const int per = (n_items + 7) >> 3, xcd = blockIdx.x & 7;
+  auto claim = [&](int i) {              // thread 0 only; -1 when every item is taken
+    const int lo = xcd * per, hi = lo + per < n_items ? lo + per : n_items;
+    if (lo + i < hi) return lo + i;
+    for (int k = 1; k < 8; ++k) {
+      const int x = (xcd + k) & 7, xl = x * per, xh = xl + per < n_items ? xl + per : n_items;
+      if (xl >= xh || __hip_atomic_load(&ctr[x], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= xh - xl) continue;
+      const int y = atomicAdd(&ctr[x], 1);
+      if (xl + y < xh) return xl + y;
+    }
+    return -1;
+  };
+  int pending = 0;
+  if (tid == 0) {
+    q_slot[2] = claim(atomicAdd(&ctr[xcd], 1));
+    q_slot[0] = claim(atomicAdd(&ctr[xcd], 1));
+    pending = atomicAdd(&ctr[xcd], 1);
+  }
+  __syncthreads();
+  const int first = __builtin_amdgcn_readfirstlane(q_slot[2]);
   if (first < 0) return;
   ScoreTile T = score_tile(a, t, first);
   set_loads(T, true);
@@ -586,8 +617,13 @@ __global__ __launch_bounds__(512, 1) void score_kernel(ScoreArgs a, SeqTable t, 
     // the next tile is decoded here, where no accumulator or fragment is
     // live (decoded mid-tile, its temporaries pushed the fp8 kernel past
     // 256 VGPRs)
-    const int nxt = score_item_at(b, nwg, n_items, j + 1);
+    const int nxt = __builtin_amdgcn_readfirstlane(q_slot[j & 1]);
     const bool has_next = nxt >= 0;
+    if (tid == 0) {
+      const int nn = has_next ? claim(pending) : -1;
+      q_slot[(j + 1) & 1] = nn;
+      if (nn >= 0) pending = atomicAdd(&ctr[xcd], 1);
+    }
     const ScoreTile Tn = has_next ? score_tile(a, t, nxt) : T;
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
@@ -678,6 +714,12 @@ __global__ __launch_bounds__(256) void score_fill_kernel(float *__restrict__ sco
   for (int J = j0 + (int)threadIdx.x; J < max_nb; J += 256) row[J] = -INFINITY;
 }
 
+size_t score_workspace_ctr_offset(int Hkv, int R) { return ((size_t)Hkv * R * sizeof(float) + 255) / 256 * 256; }
+size_t score_workspace_bytes(int Hkv, int R, int num_seqs) {
+  const size_t launches = (size_t)(num_seqs + kMaxSeqsPerLaunch - 1) / kMaxSeqsPerLaunch;
+  return score_workspace_ctr_offset(Hkv, R) + (launches * 8 * sizeof(int32_t) + 255) / 256 * 256;
+}
+
 // CUs of the stream's device (256 if the query fails).
 static int score_device_cus(hipStream_t s) {
   int dev = 0;
@@ -692,7 +734,7 @@ static int score_device_cus(hipStream_t s) {
   return cus;
 }
 
-hipError_t launch_score(const ScoreLaunch &l, const SeqTable &t, int n_items, hipStream_t s) {
+hipError_t launch_score(const ScoreLaunch &l, const SeqTable &t, int n_items, int launch_index, hipStream_t s) {
   ScoreArgs a;
   a.q = (const __bf16 *)l.q;
   a.k = (const __bf16 *)l.k;
@@ -708,16 +750,12 @@ hipError_t launch_score(const ScoreLaunch &l, const SeqTable &t, int n_items, hi
   a.scale = l.scale;
   const int rows = t.row[t.n] - t.row[0];
   hipLaunchKernelGGL(score_fill_kernel, dim3(rows, l.Hq), dim3(256), 0, s, l.scores, t, l.R, l.max_nb);
-  // persistent: one workgroup per CU (a multiple of 8), or one per item when
-  // there are no more items than that
+  // persistent: one workgroup per CU, at most one per item
   const int cus = score_device_cus(s);
-  int grid = n_items < cus ? n_items : cus;
-  if (grid < n_items) {
-    grid &= ~7;
-    if (grid < 8) grid = n_items < 8 ? n_items : 8;
-  }
-  if (l.fp8) hipLaunchKernelGGL(score_kernel<true>, dim3(grid), dim3(512), 0, s, a, t, n_items);
-  else hipLaunchKernelGGL(score_kernel<false>, dim3(grid), dim3(512), 0, s, a, t, n_items);
+  const int grid = n_items < cus ? n_items : cus;
+  int32_t *ctr = l.ctr + 8 * launch_index;
+  if (l.fp8) hipLaunchKernelGGL(score_kernel<true>, dim3(grid), dim3(512), 0, s, a, t, n_items, ctr);
+  else hipLaunchKernelGGL(score_kernel<false>, dim3(grid), dim3(512), 0, s, a, t, n_items, ctr);
   return hipGetLastError();
 }
 

@@ -75,8 +75,9 @@ const char *stem_status_string(int status) {
 size_t stem_score_workspace_bytes(const stem_problem_t *p) {
   Shape s;
   if (check_problem(p, &s) != STEM_OK) return 0;
-  // per (KV head, key block): log value norm, then the bonus (fp32)
-  return ((size_t)s.Hkv * s.R * sizeof(float) + 255) / 256 * 256;
+  // per (KV head, key block): log value norm, then the bonus (fp32); then
+  // the scoring kernel's work-queue counters
+  return score_workspace_bytes(s.Hkv, s.R, s.B);
 }
 
 }  // extern "C"
@@ -108,6 +109,8 @@ static int score_common(const stem_problem_t *p, const void *q, const void *k, c
   a.fp8 = fp8;
   a.scores = scores;
   a.ell = (float *)workspace;
+  a.ctr = (int32_t *)((uint8_t *)workspace + score_workspace_ctr_offset(s.Hkv, s.R));
+  a.n_ctr = 8 * ((s.B + kMaxSeqsPerLaunch - 1) / kMaxSeqsPerLaunch);
   a.Hq = s.Hq;
   a.Hkv = s.Hkv;
   a.R = s.R;
@@ -143,7 +146,7 @@ static int score_common(const stem_problem_t *p, const void *q, const void *k, c
     t.item[n] = (int32_t)slots;
     const int64_t items = slots * G;
     if (items >= ((int64_t)1 << 31)) return STEM_ERR_UNSUPPORTED;
-    if (launch_score(a, t, (int)items, hs) != hipSuccess) return STEM_ERR_HIP;
+    if (launch_score(a, t, (int)items, z0 / kMaxSeqsPerLaunch, hs) != hipSuccess) return STEM_ERR_HIP;
   }
   return STEM_OK;
 }

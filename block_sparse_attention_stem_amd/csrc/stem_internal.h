@@ -109,6 +109,8 @@ struct ScoreLaunch {
   const void *q, *k, *v;
   const float *q_scale, *k_scale, *v_scale;   // e4m3 inputs: per (block, head); else null
   float *scores, *ell;          // ell: workspace [Hkv][R] (log norms, then bonus)
+  int32_t *ctr;                 // workspace: 8 work-queue counters per score launch
+  int32_t n_ctr;
   int32_t Hq, Hkv, R, max_nb;
   int32_t stride, chunk_size;
   float scale, beta;
@@ -116,7 +118,10 @@ struct ScoreLaunch {
 };
 hipError_t launch_vnorm(const ScoreLaunch &a, hipStream_t s);
 hipError_t launch_vstats(const ScoreLaunch &a, const SeqTable &t, hipStream_t s);
-hipError_t launch_score(const ScoreLaunch &a, const SeqTable &t, int n_items, hipStream_t s);
+hipError_t launch_score(const ScoreLaunch &a, const SeqTable &t, int n_items, int launch_index, hipStream_t s);
+// Score workspace: ell [Hkv][R] fp32, then the counters, each part 256-byte aligned.
+size_t score_workspace_ctr_offset(int Hkv, int R);
+size_t score_workspace_bytes(int Hkv, int R, int num_seqs);
 
 struct TopkLaunch {
   const float *scores;

@@ -105,8 +105,10 @@ const char *stem_status_string(int status);
  * is the one implemented (others return UNSUPPORTED).  chunk_size is a
  * positive multiple of block_size (it orders the work, it changes no value).
  * Sequences of more than 65536 blocks (8M tokens) return UNSUPPORTED.
- * workspace: device memory of at least stem_score_workspace_bytes(p) bytes,
- * 256-byte aligned; its contents on return are unspecified.
+ * workspace: device memory of at least stem_score_workspace_bytes(p) bytes
+ * (one fp32 per KV head and key block, then 32 bytes of work-queue counters
+ * per 64 sequences, each part rounded up to 256 bytes), 256-byte aligned; its
+ * contents on return are unspecified.
  * ------------------------------------------------------------------------- */
 size_t stem_score_workspace_bytes(const stem_problem_t *p);
 int stem_score(const stem_problem_t *p, const void *q, const void *k, const void *v,
@@ -116,10 +118,12 @@ int stem_score(const stem_problem_t *p, const void *q, const void *k, const void
 /* stem_score for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
  * same computation and result as stem_score, with the library's own device
- * array of STEM_SCORE_SCRATCH_BYTES (1 MiB, one per GPU, held until the
- * process ends) in place of the workspace argument: enough for
- * num_kv_heads * R <= 262144 (e.g. 8 KV heads and 4M tokens).  Larger
- * problems return STEM_ERR_WORKSPACE before anything is enqueued.  The call
+ * array of STEM_SCORE_SCRATCH_BYTES (1 MiB + 4 KiB, one per GPU, held until
+ * the process ends) in place of the workspace argument: it serves every
+ * problem whose stem_score_workspace_bytes fits, which includes all with
+ * num_kv_heads * R <= 262144 (e.g. 8 KV heads and 4M tokens) and at most
+ * 8192 sequences.  Larger problems return STEM_ERR_WORKSPACE before
+ * anything is enqueued.  The call
  * allocates nothing; its first call on a GPU (the device of `stream`, or the
  * current device for the null stream) looks up that GPU's array address
  * (hipGetSymbolAddress), so a caller that will capture should make one call
@@ -127,7 +131,7 @@ int stem_score(const stem_problem_t *p, const void *q, const void *k, const void
  * calls that overlap on one GPU (different streams, threads or graphs in
  * flight together) race and must be serialised by the caller.  The array's
  * contents are rewritten by every call before they are read. */
-#define STEM_SCORE_SCRATCH_BYTES (1u << 20)
+#define STEM_SCORE_SCRATCH_BYTES ((1u << 20) + 4096u)
 int stem_score_noalloc(const stem_problem_t *p, const void *q, const void *k, const void *v,
                        int32_t stride, int32_t chunk_size, float norm, float beta,
                        float *scores, void *stream);

@@ -99,7 +99,9 @@ def test_score_argument_errors():
     assert _score(stem.Problem([0, 1024], 4, 2, block_size=64)) == 2
     assert _score(stem.Problem([0, 1024, 1024], 4, 2)) == 1   # empty sequence
     assert _score(stem.Problem([0, 128 * 65537], 4, 2), wsb=1 << 30) == 2   # longer than 65536 blocks
-    assert stem.stem_score_workspace_bytes(stem.Problem([0, 1024], 4, 2)) == 256
+    # 2 x 8 fp32 block values, then 8 queue counters, each part padded to 256 bytes
+    assert stem.stem_score_workspace_bytes(stem.Problem([0, 1024], 4, 2)) == 512
+    assert stem.stem_score_workspace_bytes(stem.Problem([0] + [128 * (i + 1) for i in range(65)], 4, 2)) == 1024   # 520 -> 768, two launches of counters -> 256
     # e4m3 scoring: every scale pointer is required; the rest as stem_score
     lib = stem.load_library()
     p = stem.Problem([0, 1024], 4, 2)
@@ -246,7 +248,7 @@ int main(void) {
   if (strcmp(stem_status_string(STEM_ERR_CAPACITY), "STEM_ERR_CAPACITY") != 0) return 1;
   if (stem_tpd_budget(0, 8, 10.0, 0.5, 1.0) != 10) return 2;
   if (stem_max_kept(&p, &ks, 0.5, 1.0, 1, 1) != 8) return 3;
-  if (stem_score_workspace_bytes(&p) != 256) return 4;
+  if (stem_score_workspace_bytes(&p) != 512) return 4;
   /* a null q is rejected before anything touches a device */
   if (stem_score(&p, NULL, NULL, NULL, 8, 2048, 1.0f, 0.2f, NULL, NULL, 0, NULL) != STEM_ERR_INVALID_ARG) return 5;
   printf("ok\n");
@@ -263,14 +265,19 @@ int main(void) {
 
 def test_noalloc_score_rejects_problems_beyond_its_scratch():
     """stem_score_noalloc checks the problem against its fixed scratch array
-    before touching the device: Hkv * R floats must fit in
-    STEM_SCORE_SCRATCH_BYTES, else STEM_ERR_WORKSPACE (no launch, no GPU)."""
+    before touching the device: the score workspace (Hkv * R floats, then the
+    work-queue counters) must fit in STEM_SCORE_SCRATCH_BYTES, else
+    STEM_ERR_WORKSPACE (no launch, no GPU)."""
     lib = stem.load_library()
-    assert stem.STEM_SCORE_SCRATCH_BYTES == 1 << 20
+    assert stem.STEM_SCORE_SCRATCH_BYTES == (1 << 20) + 4096
+    # the documented guarantee: Hkv * R <= 262144 with at most 8192 sequences fits
+    assert stem.stem_score_workspace_bytes(stem.Problem([0, 128 * 32768], 8, 8)) <= stem.STEM_SCORE_SCRATCH_BYTES
+    many = stem.Problem([128 * i for i in range(8193)], 32, 32)      # 8192 one-block sequences, R * Hkv = 262144
+    assert stem.stem_score_workspace_bytes(many) <= stem.STEM_SCORE_SCRATCH_BYTES
     dummy = ctypes.c_void_p(256)
-    for Hkv, nblk, ok in ((64, 4097, False), (8, 32769, False)):
+    for Hkv, nblk in ((64, 4113), (8, 32897)):
         p = stem.Problem([0, 128 * nblk], Hkv, Hkv)
-        assert Hkv * nblk * 4 > stem.STEM_SCORE_SCRATCH_BYTES
+        assert stem.stem_score_workspace_bytes(p) > stem.STEM_SCORE_SCRATCH_BYTES
         st = lib.stem_score_noalloc(p.ref, dummy, dummy, dummy, 8, 2048, 1.0, 0.2, dummy, None)
         assert st == 4, stem.STATUS.get(st, st)                  # STEM_ERR_WORKSPACE
     # invalid problems are rejected as in stem_score
