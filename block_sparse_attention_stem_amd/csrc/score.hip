@@ -171,14 +171,17 @@ hipError_t launch_vstats(const ScoreLaunch &a, const SeqTable &t, hipStream_t s)
 // permutation is applied on the global side of the loads (each lane fetches
 // the piece that belongs at its fixed LDS slot).
 //
-// The grid is persistent: one workgroup per CU walks a fixed list of tiles
-// (XCD-local, see score_item_at), and the ring runs on across tiles: the
-// last steps of a tile request the first chunks of the next one, so a tile's
-// load latency, epilogue and dispatch no longer leave the matrix core idle
-// (measured against one workgroup per tile, same box, identical scores:
-// 128K layer 7.41 against 7.59 ms, 64K 1.91 against 2.02, the fp8 varlen
-// layer 3.07 against 3.35 on bf16 and 1.55 against 2.07 on e4m3 codes).
-// The tile-independent -inf entries of S are written by score_fill_kernel.
+// The grid is persistent: one workgroup per CU takes tiles from a work
+// queue per XCD (stealing from the other XCDs at the end), and the ring runs
+// on across tiles: the last steps of a tile request the first chunks of the
+// next one, so a tile's load latency, epilogue and dispatch no longer leave
+// the matrix core idle.  Measured on one box with identical scores, against
+// one workgroup per tile and against a fixed XCD-local tile list per
+// workgroup: 128K layer 6.91 / 7.59 / 7.46 ms, 64K 1.80 / 1.99 / 1.90, the
+// fp8 varlen layer 2.90 / 3.34 / 3.08 on bf16 and 1.52 / 2.06 / 1.60 on e4m3
+// codes (the fixed list loses to the queue on the CUs and XCDs that run
+// slower).  The tile-independent -inf entries of S are written by
+// score_fill_kernel.
 //
 // e4m3 inputs (kFp8): the same tile, rows and loads; a chunk is 64 codes
 // (one 64-byte piece of one token row, 16 chunks), one 32x32x64 fp8 MFMA step
