@@ -28,6 +28,10 @@ HIPFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-ffp-contract=fast", "-munsafe-fp-atomics",
+    # Atomics keep their plain form: the optimizer that turns a one-lane atomic
+    # into a wave-wide one broadcasts its result at once, which makes the
+    # work-queue claims wait for every load in flight.
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

@@ -398,8 +398,9 @@ constexpr int kRowVh = 72;                       // V^T half row: 64 keys + pad 
 constexpr int kHalfV = kHeadDim * kRowVh;        // V^T half: 128 dims x 9 chunks (elements)
 constexpr uint32_t kBufWord3 = 0x00020000u;      // raw buffer descriptor word 3 (gfx9 dword access)
 
-template <bool kSparse, bool kPair>
-__device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTable &t, int rows, int item) {
+template <bool kSparse, bool kPair, typename Claim>
+__device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTable &t, int rows, int item,
+                                               Claim &&claim) {
   static_assert(kSparse || !kPair, "paired lists are block-sparse");
   __shared__ __attribute__((aligned(1024))) uint16_t K0[2 * kHalfK];   // bf16 K halves, [key][d]
   __shared__ __attribute__((aligned(1024))) uint16_t V0[2 * kHalfV];   // fp16 V^T halves, [d][key]
@@ -433,7 +434,18 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
   cint32 *list = kSparse ? as_const(a.idx) + lrow * a.k_cap : nullptr;
   // Lists are trusted to be ascending in [0, I]; counts and ids are still
   // clamped so a malformed list can never address outside the sequence.
+  // The first entry is read beside the count (a list row always has k_cap
+  // entries, so it exists even when the count is 0) and Q is requested
+  // before either arrives: a row then starts after one scalar round trip
+  // and one tile fetch, not three dependent fetches.
   int n_blk = kSparse ? as_const(a.cnt)[lrow] : w.I + 1;
+  const int first_entry = kSparse && !kPair ? list[0] : 0;
+  bf16x8 qf[8];            // Q as the B operand: query qloc, head dims 16 ks + 8 lg .. +7
+  {
+    const __bf16 *qrow = (const __bf16 *)a.q + (qtok * a.Hq + w.h) * kHeadDim + 8 * lg;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(ld16(qrow + 16 * ks));
+  }
   if (kSparse && n_blk > a.k_cap) n_blk = a.k_cap;
   int n_b = 0;
   if constexpr (kPair) {
@@ -446,6 +458,9 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
   float *lse = a.lse ? a.lse + (size_t)w.h * a.T + qtok : nullptr;
   if (n_blk + n_b <= 0) {
     if (ck == 0) write_empty(orow, lse, lg);
+    block_sync();
+    claim();
+    block_sync();
     return;
   }
   auto clampJ = [&](int J) { return J < 0 ? 0 : (J > w.I ? w.I : J); };
@@ -499,14 +514,6 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
   };
   auto blk = [&](int b) __attribute__((always_inline)) { return blk_entry(b) & 0xffff; };
   const int my_bit = grp == 0 ? 1 : 2;
-
-  // Q as the B operand: query qloc, head dims 16 ks + 8 lg .. +7
-  bf16x8 qf[8];
-  {
-    const __bf16 *qrow = (const __bf16 *)a.q + (qtok * a.Hq + w.h) * kHeadDim + 8 * lg;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(ld16(qrow + 16 * ks));
-  }
 
   // Direct loads through raw buffer descriptors rebased per block (32-bit
   // per-lane offsets, scalar bases).  Load instruction k of a half writes
@@ -762,10 +769,11 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
   };
 
   if constexpr (kPair) own = blk_entry(0);
-  int J = blk(0);
+  int J = kPair ? blk(0) : (kSparse ? clampJ(first_entry) : 0);
   issue_k(J, K0);
   if (grp == 1) block_sync();        // group 1 runs one phase behind
   step(NoPV{}, 0, J, K0, V1, K1, V0);
+  claim();
   int b = 1;
   while (b < n_blk) {
     step(WithPV{}, b, J, K1, V0, K0, V1);
@@ -780,21 +788,31 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
   if (grp == 0) block_sync();        // realign the groups
 
   // merge the two key halves: the key-half-1 wave of each query slice (ck = 1)
-  // hands (O, m, l) to its key-half-0 partner through LDS
+  // hands (O, m, l) to its key-half-0 partner through LDS.  Each lane's 66
+  // values form one row of 68 floats (272 bytes, so the 16 lanes of a 16-byte
+  // access hit distinct banks), written and read in 16-byte pieces; the
+  // reader issues all of its reads before it uses any, so their latencies
+  // overlap (one register reused for every read had them run one by one).
   block_sync();
-  float *xch = (float *)(cq < 2 ? K0 : K1) + (cq & 1) * (66 * 64);
+  constexpr int kXRow = 68;
+  float *xrow = (float *)(cq < 2 ? K0 : K1) + (cq & 1) * (64 * kXRow) + lane * kXRow;
   if (ck == 1) {
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xch[(16 * u + i) * 64 + lane] = o[u][i];
-    xch[64 * 64 + lane] = m_run;
-    xch[65 * 64 + lane] = l_run;
+      for (int j = 0; j < 4; ++j)
+        st16(xrow + 16 * u + 4 * j, u32x4{__float_as_uint(o[u][4 * j]), __float_as_uint(o[u][4 * j + 1]),
+                                          __float_as_uint(o[u][4 * j + 2]), __float_as_uint(o[u][4 * j + 3])});
+    st8(xrow + 64, u32x2{__float_as_uint(m_run), __float_as_uint(l_run)});
   }
   block_sync();
   if (ck == 0) {
+    u32x4 xo[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) xo[k] = ld16(xrow + 4 * k);
+    const u32x2 ml = *reinterpret_cast<const u32x2 *>(xrow + 64);
     // the merged max is finite: the key equal to the query is visible in one half
-    const float m1 = xch[64 * 64 + lane], l1 = xch[65 * 64 + lane];
+    const float m1 = __uint_as_float(ml[0]), l1 = __uint_as_float(ml[1]);
     const float m = fmaxf(m_run, m1);
     const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
     const float a1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - m);
@@ -805,7 +823,7 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
 #pragma unroll
     for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[u][i] = (o[u][i] * a0 + xch[(16 * u + i) * 64 + lane] * a1) * inv;
+      for (int i = 0; i < 16; ++i) o[u][i] = (o[u][i] * a0 + __uint_as_float(xo[4 * u + (i >> 2)][i & 3]) * a1) * inv;
     stage_out(V0, o, qloc, lg);
     if (lse && lg == 0) *lse = kPair && !(l > 0.f) ? -INFINITY : (m + __log2f(l)) * 0.69314718055994531f;
   }
@@ -824,10 +842,15 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
 // speed (up to 6 % apart on identical work), and with one item per
 // workgroup, dispatched round-robin over the XCDs, the fast ones idled for
 // up to 1.5 ms at the end of a 33 ms call; a workgroup also no longer pays a
-// dispatch per item.  The next item's counter is bumped when an item starts
-// and read when it ends, so the atomic's latency hides under the item.
-// The persistent item loop shared by the attention kernels: runs item(i)
-// for every item i in [0, n) that this workgroup claims (see above).
+// dispatch per item.  The next item's counter is bumped when an item starts,
+// and the item resolves it into the next item (thread 0 writes it to LDS)
+// once its first step has waited for its loads, so the atomic's latency
+// hides under that step and the item's end needs no extra barrier.
+// The persistent item loop shared by the attention kernels: runs
+// item(i, claim) for every item i in [0, n) that this workgroup claims.  The
+// item calls claim() once, with every thread, after one of its barriers and
+// before its last one: the barrier before it orders every wave's read of the
+// current next_item ahead of the write, the one after it publishes the write.
 template <typename F>
 __device__ __forceinline__ void run_items(int n, int32_t *ctr, F &&item) {
   __shared__ int32_t next_item;
@@ -848,20 +871,22 @@ __device__ __forceinline__ void run_items(int n, int32_t *ctr, F &&item) {
   if (threadIdx.x == 0) next_item = own_or_steal(atomicAdd(&ctr[xcd], 1));
   __syncthreads();
   int cur = next_item;
+  // Declared outside the loop: a fresh zero at the top of each item would be
+  // a write to the register the previous claim's atomic returns into, which
+  // the compiler guards with a wait for every outstanding memory operation.
+  int pending = 0;
   while (cur >= 0) {
-    int pending = 0;
     if (threadIdx.x == 0) pending = atomicAdd(&ctr[xcd], 1);
-    item(cur);
-    block_sync();                    // every wave is past its last read of next_item and the item's LDS
-    if (threadIdx.x == 0) next_item = own_or_steal(pending);
-    block_sync();
+    item(cur, [&]() __attribute__((always_inline)) {
+      if (threadIdx.x == 0) next_item = own_or_steal(pending);
+    });
     cur = __builtin_amdgcn_readfirstlane(next_item);
   }
 }
 
 template <bool kSparse, bool kPair>
 __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTable t, int rows, int32_t *ctr) {
-  run_items(rows * a.Hq, ctr, [&](int i) { attn_bf16_item<kSparse, kPair>(a, t, rows, i); });
+  run_items(rows * a.Hq, ctr, [&](int i, auto &&claim) { attn_bf16_item<kSparse, kPair>(a, t, rows, i, claim); });
 }
 
 // ====================================================================== fp8
@@ -900,8 +925,9 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64_bs(i32x8 a, i32x8 b, f32x16 
 }
 
 
-template <bool kSparse, bool kPV16>
-__device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTable &t, int rows, int item) {
+template <bool kSparse, bool kPV16, typename Claim>
+__device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTable &t, int rows, int item,
+                                              Claim &&claim) {
   __shared__ __attribute__((aligned(1024))) uint8_t Ks[kTile8];      // e4m3 K, [key][d], padded rows
   __shared__ __attribute__((aligned(1024))) uint8_t Vs[kTile8];      // e4m3 V^T image (unused with kPV16)
   __shared__ __attribute__((aligned(1024))) uint16_t Vh[kTile16];    // fp16 V^T image (diagonal; output staging)
@@ -922,6 +948,9 @@ __device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTabl
   float *lse = a.lse ? a.lse + (size_t)w.h * a.T + qtok : nullptr;
   if (n_blk <= 0) {
     write_empty(orow, lse, lg);
+    block_sync();
+    claim();
+    block_sync();
     return;
   }
   auto clampJ = [&](int x) { return x < 0 ? 0 : (x > w.I ? w.I : x); };
@@ -1125,6 +1154,7 @@ __device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTabl
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[u][i] *= inv;
   block_sync();                      // every wave's last P.V has read Vh
+  claim();
   stage_out(Vh, o, qloc, lg);
   if (lse && lg == 0) *lse = (R - kFp8Off + __log2f(l_tot)) * 0.69314718055994531f;
   block_sync();
@@ -1134,7 +1164,7 @@ __device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTabl
 // Persistent like the bf16 kernel (run_items), two workgroups per CU.
 template <bool kSparse, bool kPV16>
 __global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable t, int rows, int32_t *ctr) {
-  run_items(rows * a.Hq, ctr, [&](int i) { attn_fp8_item<kSparse, kPV16>(a, t, rows, i); });
+  run_items(rows * a.Hq, ctr, [&](int i, auto &&claim) { attn_fp8_item<kSparse, kPV16>(a, t, rows, i, claim); });
 }
 
 // ================================================================ launchers
