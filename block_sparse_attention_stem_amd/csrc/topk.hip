@@ -71,6 +71,15 @@ template <int MC>
 __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int32_t *__restrict__ orow,
                                          int32_t *__restrict__ ocnt, int k_cap, int I, int sink_end, int win0,
                                          int need, int n_cand, int lane) {
+  // Every slot's score is requested before any is used (slots past the row
+  // re-read entry I, which exists): loads placed inside the per-slot
+  // conditions below were each awaited before the next one was issued.
+  float sv[MC];
+#pragma unroll
+  for (int m = 0; m < MC; ++m) {
+    const int J = lane + 64 * m;
+    sv[m] = srow[J <= I ? J : I];
+  }
   uint32_t key[MC];
   uint32_t forced = 0;                             // bit m: forced block
   uint32_t kmax = 0u, kmin = 0xffffffffu;
@@ -81,7 +90,7 @@ __device__ __forceinline__ void topk_row(const float *__restrict__ srow, int32_t
     if (J <= I) {
       if ((J < sink_end) || (J >= win0)) forced |= 1u << m;
       else {
-        key[m] = order_key(srow[J]);
+        key[m] = order_key(sv[m]);
         kmax = key[m] > kmax ? key[m] : kmax;
         kmin = key[m] < kmin ? key[m] : kmin;
       }
