@@ -844,8 +844,9 @@ __device__ __forceinline__ void attn_bf16_item(const AttnLaunch &a, const SeqTab
 // up to 1.5 ms at the end of a 33 ms call; a workgroup also no longer pays a
 // dispatch per item.  The next item's counter is bumped when an item starts,
 // and the item resolves it into the next item (thread 0 writes it to LDS)
-// once its first step has waited for its loads, so the atomic's latency
-// hides under that step and the item's end needs no extra barrier.
+// later on (the bf16 kernel after its first step, the fp8 kernel at the
+// barrier that ends its block loop), so the atomic's latency hides under the
+// item and the item's end needs no barrier of its own.
 // The persistent item loop shared by the attention kernels: runs
 // item(i, claim) for every item i in [0, n) that this workgroup claims.  The
 // item calls claim() once, with every thread, after one of its barriers and
