@@ -155,6 +155,49 @@ def test_empty_lists_give_zero_and_minus_inf(varlen):
     assert bool((out == 0).all()) and bool(torch.isneginf(lse).all())
 
 
+def _empty_some_rows(idx, cnt, seed):
+    """The same lists with a seeded third of the (head, row) lists emptied."""
+    g = torch.Generator().manual_seed(seed)
+    drop = torch.rand(cnt.shape, generator=g) < 1.0 / 3.0
+    ci, ii = cnt.cpu().clone(), idx.cpu().clone()
+    ci[drop] = 0
+    ii[drop] = -1
+    return ii, ci
+
+
+def test_empty_rows_between_full_ones(varlen, fp8_small):
+    """A third of the rows with empty lists, spread among full ones, so the
+    persistent workgroups pass from empty rows to full ones and back: bf16,
+    e4m3 weights and fp16 weights against the oracle on the same lists
+    (an empty row gives 0 and lse -inf)."""
+    lens, (q, k, v), (qf, kf, vf) = varlen
+    cu = S.cu_from_lengths(lens)
+    p = stem.Problem(cu, 4, 2)
+    qd, kd, vd = to_dev(q, k, v)
+    s = stem.stem_score(p, qd, kd, vd)
+    idx, cnt = stem.stem_schedule_topk(p, s, [3, 5, 1, 6], 0.5, 1.0, 1, 1)
+    ii, ci = _empty_some_rows(idx, cnt, 31)
+    assert 0 < int((ci == 0).sum()) < ci.numel()
+    out, lse = stem.stem_bsa_prefill(p, qd, kd, vd, ii.to(dev()), ci.to(dev()), SCALE, want_lse=True)
+    ro, rl = O.block_sparse_attention(qf, kf, vf, ii.numpy(), ci.numpy(), cu, 4, 2, SCALE)
+    check_out(f64(out), ro, BF16_MAX_ABS, BF16_MEAN_REL, "bf16 with empty rows")
+    check_lse(lse.cpu().numpy().astype(np.float64), rl, "bf16 with empty rows")
+
+    lens8, _, (q8, k8, v8), (qs, ks, vs), (qf8, kf8, vf8) = fp8_small
+    cu8 = S.cu_from_lengths(lens8)
+    p8 = stem.Problem(cu8, 4, 2)
+    s8 = stem.stem_score(p8, *to_dev(*fp8_small[1]))
+    idx8, cnt8 = stem.stem_schedule_topk(p8, s8, [1, 3, 4], 0.5, 1.0, 1, 1)
+    ii8, ci8 = _empty_some_rows(idx8, cnt8, 32)
+    assert 0 < int((ci8 == 0).sum()) < ci8.numel()
+    ro8, _ = O.block_sparse_attention(qf8, kf8, vf8, ii8.numpy(), ci8.numpy(), cu8, 4, 2, SCALE)
+    sc = to_dev(qs, ks, vs)
+    for fp16_weights in (False, True):
+        o8 = stem.stem_bsa_prefill(p8, *to_dev(q8, k8, v8), ii8.to(dev()), ci8.to(dev()), SCALE, scales=sc,
+                                   fp16_weights=fp16_weights)
+        check_out(f64(o8), ro8, FP8_MAX_ABS, None, f"fp8 with empty rows, fp16_weights={fp16_weights}")
+
+
 def test_chunk_size_changes_no_score(varlen):
     lens, (q, k, v), _ = varlen
     p = stem.Problem(S.cu_from_lengths(lens), 4, 2)

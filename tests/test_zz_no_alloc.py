@@ -34,3 +34,10 @@ def test_noalloc_scores_equal_workspace_scores_on_two_calls():
     # the second call is smaller: every entry it reads must have been rewritten by it
     _one((1280, 640, 384), 8, 2, seed=21, beta=0.2)
     _one((512,), 4, 1, seed=22, beta=0.5)
+
+
+def test_noalloc_scores_on_more_sequences_than_one_launch_takes():
+    # 72 sequences: two launches of the score kernel, each with its own work-queue
+    # counters in the scratch array, then a one-launch call again
+    _one((128,) * 40 + (256,) * 30 + (384, 128), 4, 2, seed=23, beta=0.2)
+    _one((640, 128), 4, 2, seed=24, beta=0.2)
