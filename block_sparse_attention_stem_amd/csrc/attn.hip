@@ -134,8 +134,8 @@ __global__ __launch_bounds__(256) void vprep_bf16_kernel(const __bf16 *__restric
   if (tid < kBlock) st16(out + tid * kRow16 + kHeadDim, u32x4{0u, 0u, 0u, 0u});   // pad chunk
 }
 
-// fp8: writes the e4m3 V^T image (16 KB per block) and an fp16 V^T image
-// (32 KB per block, exact) used when the block is a row's diagonal block.
+// fp8: writes the e4m3 V^T image (16 KB per block) and, unless img16 is null,
+// an fp16 V^T image (32 KB per block, exact) for the fp16-weight kernel.
 // Block kb (global key-block row, the image index) starts at token tb of v.
 __device__ __forceinline__ void vprep_fp8_block(const uint8_t *__restrict__ v, size_t tb, int kb, int g,
                                                 uint8_t *__restrict__ img8, uint16_t *__restrict__ img16,
@@ -163,6 +163,7 @@ __device__ __forceinline__ void vprep_fp8_block(const uint8_t *__restrict__ v, s
     st16(o8 + d * kRow8 + 16 * ch, u32x4{w4[0], w4[1], w4[2], w4[3]});
   }
   if (tid < kBlock) st16(o8 + tid * kRow8 + kHeadDim, u32x4{0u, 0u, 0u, 0u});
+  if (img16 == nullptr) return;
   uint16_t *o16 = img16 + ((size_t)g * R + kb) * kTile16;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
@@ -342,11 +343,10 @@ __device__ __forceinline__ float softmax_fp8(f32x16 (&s)[4], bool diag, int qloc
 }
 
 // Whether the block is heavy for this query (see softmax_fp8): its largest
-// weight 2^(cm - R + kFp8Off) (L units) is more than kHeavy of the weight sum
-// of both halves of the query so far.
+// weight 2^(cm - R + kFp8Off) (L units) is more than kHeavy of l_tot, the
+// query's weight sum so far (both lane halves).
 constexpr float kHeavy = 0.125f;
-__device__ __forceinline__ bool heavy_block(float cm, float R, float L) {
-  const float l_tot = L + __shfl_xor(L, 32, 64);
+__device__ __forceinline__ bool heavy_block(float cm, float R, float l_tot) {
   return __builtin_amdgcn_exp2f(cm - R + kFp8Off) > kHeavy * l_tot;
 }
 
@@ -891,17 +891,15 @@ __global__ __launch_bounds__(512, 1) void attn_bf16_kernel(AttnLaunch a, SeqTabl
 }
 
 // ====================================================================== fp8
-// Same pipeline on e4m3 operands with the 32x32x64 fp8 MFMA: Q.K^T in two
-// K=64 steps per key tile, P quantised to e4m3 (at most 430 < 448, see
-// softmax_fp8), P.V in two K=64 steps per head-dim tile.  Per-block scales:
-// the q and k scales fold into the exponent scale c of the block, the v
-// scale into the exponent offset of the weights (softmax_fp8), so no
-// per-element multiply is spent on either.  The diagonal block, where the
-// first queries of a sequence see only a few keys and 3-bit weights would not
-// average out, runs its P.V in fp16 from the exact fp16 V^T image.  kPV16
-// runs every block's P.V that way (fp16 weights, 11 significant bits): the
-// e4m3 V^T tile is then never loaded, and a row whose attention sits on a few
-// keys keeps bf16-level accuracy, at the price of twice the P.V MFMA time.
+// e4m3 operands with the 32x32x64 fp8 MFMA: Q.K^T in two K=64 steps per key
+// tile, P.V in K=64 steps per head-dim tile.  Per-block scales: the q and k
+// scales fold into the exponent scale c of the block, the v scale into the
+// exponent offset of the weights (softmax_fp8), so no per-element multiply is
+// spent on either.  Two kernels: attn_fp8_kernel rounds the weights to e4m3
+// (at most 430 < 448, see softmax_fp8) and adds a second e4m3 pass with the
+// rounding residual where a block holds a large share of a query's weight;
+// attn_fp8_pv16_kernel keeps every weight in fp16 (11 significant bits) and
+// runs P.V on the fp16 V^T image, at the price of twice the P.V MFMA time.
 __device__ __forceinline__ uint32_t pack_fp8x4(float a, float b, float c, float d) {
   uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0u, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
@@ -926,12 +924,11 @@ __device__ __forceinline__ f32x16 mfma_fp8_32x32x64_bs(i32x8 a, i32x8 b, f32x16 
 }
 
 
-template <bool kSparse, bool kPV16, typename Claim>
-__device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTable &t, int rows, int item,
-                                              Claim &&claim) {
+template <bool kSparse, typename Claim>
+__device__ __forceinline__ void attn_fp8_pv16_item(const AttnLaunch &a, const SeqTable &t, int rows, int item,
+                                                   Claim &&claim) {
   __shared__ __attribute__((aligned(1024))) uint8_t Ks[kTile8];      // e4m3 K, [key][d], padded rows
-  __shared__ __attribute__((aligned(1024))) uint8_t Vs[kTile8];      // e4m3 V^T image (unused with kPV16)
-  __shared__ __attribute__((aligned(1024))) uint16_t Vh[kTile16];    // fp16 V^T image (diagonal; output staging)
+  __shared__ __attribute__((aligned(1024))) uint16_t Vh[kTile16];    // fp16 V^T image (P.V; output staging)
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lg = lane >> 5, l32 = lane & 31;
@@ -978,7 +975,7 @@ __device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTabl
 
   // Direct loads as in the bf16 kernel.  An fp8 tile is 18 instructions
   // (slot s = 64 k + lane holds chunk s % 9 of row s / 9; chunk 8 is the pad),
-  // 5 for waves 0-1 and 4 for waves 2-3; the fp16 diagonal image is 34.
+  // 5 for waves 0-1 and 4 for waves 2-3; the fp16 V^T image is 34.
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int nk8 = wv < 2 ? 5 : 4, nk16 = wv < 2 ? 9 : 8;
   const size_t kstride = (size_t)a.Hkv * kHeadDim;
@@ -990,20 +987,12 @@ __device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTabl
     koff[m] = (uint32_t)(r * kstride + 16 * (ch < 8 ? ch : 0));
   }
   const uint8_t *kbase = kp + (size_t)w.g * kHeadDim;
-  const uint8_t *v8base = a.vimg8 + ((size_t)w.g * a.R + zrow) * kTile8 + lane * 16;
   const uint16_t *v16base = a.vimg16 + ((size_t)w.g * a.R + zrow) * kTile16 + lane * 8;
   auto issue_k = [&](int J) __attribute__((always_inline)) {
     const uint8_t *src = kbase + (size_t)srow(J) * kBlock * kstride;
 #pragma unroll
     for (int m = 0; m < 5; ++m)
       if (m < nk8) __builtin_amdgcn_global_load_lds(src + koff[m], lds_ptr(Ks + (wv + 4 * m) * 1024), 16, 0, 0);
-  };
-  auto issue_v8 = [&](int J) __attribute__((always_inline)) {
-    const uint8_t *src = v8base + (size_t)J * kTile8;
-#pragma unroll
-    for (int m = 0; m < 5; ++m)
-      if (m < nk8)
-        __builtin_amdgcn_global_load_lds(src + (wv + 4 * m) * 1024, lds_ptr(Vs + (wv + 4 * m) * 1024), 16, 0, 0);
   };
   auto issue_v16 = [&](int J) __attribute__((always_inline)) {
     const uint16_t *src = v16base + (size_t)J * kTile16;
@@ -1014,7 +1003,6 @@ __device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTabl
   };
   // Operand reads: 32 bytes = chunks 4 k + 2 lg and +1 of row 32 t + l32.
   const uint8_t *k8ad = &Ks[l32 * kRow8 + 32 * lg];
-  const uint8_t *v8ad = &Vs[l32 * kRow8 + 32 * lg];
   const uint16_t *vhad = &Vh[l32 * kRow16 + 8 * lg];
   auto ld32 = [](const uint8_t *p) __attribute__((always_inline)) {
     const u32x4 lo = ld16(p), hi = ld16(p + 16);
@@ -1028,18 +1016,9 @@ __device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTabl
 
   // One step per listed block J: K of J is in flight when it starts.  The
   // first barrier publishes K of J and marks every wave's P.V of the previous
-  // block done, so V of J (the fp16 image for the diagonal block or under
-  // kPV16, else the e4m3 one) is requested there and lands during Q.K^T and
-  // the softmax; the second barrier publishes it and frees the K tile for the
-  // next block's K, which lands during P.V.
-  //
-  // A wave for which the block is heavy (see softmax_fp8) runs a second
-  // e4m3 P.V pass with the rounding residual of its weights (pack_lo_fp8x4,
-  // same V tile): its weights then carry about 2^-8 relative error instead
-  // of 2^-4.  On spread-out attention this is the
-  // first few blocks of a row at most; on concentrated attention it is the
-  // blocks that hold the row's weight.  The decision is per wave (its 32
-  // queries) and needs no exchange.
+  // block done, so the fp16 V^T image of J is requested there and lands
+  // during Q.K^T and the softmax; the second barrier publishes it and frees
+  // the K tile for the next block's K, which lands during P.V.
   //
   // The k and v scales of a block are read one step ahead by scalar loads
   // issued between that step's Q.K^T and its softmax, which waits on no LDS
@@ -1049,13 +1028,12 @@ __device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTabl
   cfloat *ksc_c = (cfloat *)a.k_scale + (size_t)zrow * a.Hkv + w.g;
   cfloat *vsc_c = (cfloat *)a.v_scale + (size_t)zrow * a.Hkv + w.g;
   float ksc, vsc;                    // scales of the current block
-  // kDiag: the diagonal block (causal mask, fp16 weights; always a row's
-  // last block).  Otherwise has_next says whether a next block Jn follows.
+  // kDiag: the diagonal block (causal mask; always a row's last block).  Otherwise has_next says whether a next block Jn follows.
   auto step = [&](auto kDiag, int J, int Jn, bool has_next) __attribute__((always_inline)) {
     constexpr bool diag = decltype(kDiag)::value;
     wait_vmcnt<0>();
     block_sync();
-    if (kPV16 || diag) issue_v16(J); else issue_v8(J);
+    issue_v16(J);
     const float c = cq * ksc;
     // a zero V scale (an all-zero block) is taken as 2^-64: its weights still
     // count in L, and its codes contribute nothing measurable
@@ -1072,60 +1050,19 @@ __device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTabl
       ksc = ksc_c[(size_t)Jn * a.Hkv];
       vsc = vsc_c[(size_t)Jn * a.Hkv];
     }
-    const float cm = softmax_fp8(s, diag, qloc, lg, c, __builtin_amdgcn_logf(vs), __builtin_amdgcn_rcpf(vs), R, L, o);
+    softmax_fp8(s, diag, qloc, lg, c, __builtin_amdgcn_logf(vs), __builtin_amdgcn_rcpf(vs), R, L, o);
     wait_vmcnt<0>();
     block_sync();
     if (has_next) issue_k(Jn);
-    if (!kPV16 && !diag) {
-      // the heavy test runs here, behind the barrier, beside the packing
-      const bool heavy = __any(heavy_block(cm, R, L));
-      // P' packed to e4m3 (and, heavy, its residual) before any MFMA, so the
-      // fp32 weights die here; the residual pass repeats the MFMA stream on
-      // the same V tile
-      i32x8 pkh[2], pkl[2];
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
+    for (int cc = 0; cc < 8; ++cc) {
+      const int tt = cc >> 1, j0 = 8 * (cc & 1);
+      const u32x4 v4 = {pack_f16x2(s[tt][j0 + 0], s[tt][j0 + 1]), pack_f16x2(s[tt][j0 + 2], s[tt][j0 + 3]),
+                        pack_f16x2(s[tt][j0 + 4], s[tt][j0 + 5]), pack_f16x2(s[tt][j0 + 6], s[tt][j0 + 7])};
+      const f16x8 pk = as_f16x8(v4);
 #pragma unroll
-        for (int aa = 0; aa < 2; ++aa)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const f32x16 &st = s[2 * cc + aa];
-            pkh[cc][4 * aa + j] = (int)pack_fp8x4(st[4 * j + 0], st[4 * j + 1], st[4 * j + 2], st[4 * j + 3]);
-          }
-      if (heavy) {
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int aa = 0; aa < 2; ++aa)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const f32x16 &st = s[2 * cc + aa];
-              pkl[cc][4 * aa + j] = (int)pack_lo_fp8x4(st[4 * j + 0], st[4 * j + 1], st[4 * j + 2], st[4 * j + 3]);
-            }
-      }
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          o[u] = mfma_fp8_32x32x64_bs(ld32(v8ad + 32 * kRow8 * u + 64 * cc), pkh[cc], o[u], 127);
-      if (heavy) {      // the residual pass
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-          for (int u = 0; u < 4; ++u)
-            o[u] = mfma_fp8_32x32x64_bs(ld32(v8ad + 32 * kRow8 * u + 64 * cc), pkl[cc], o[u], 127);
-      }
-    } else {
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
-        const int tt = cc >> 1, j0 = 8 * (cc & 1);
-        const u32x4 v4 = {pack_f16x2(s[tt][j0 + 0], s[tt][j0 + 1]), pack_f16x2(s[tt][j0 + 2], s[tt][j0 + 3]),
-                          pack_f16x2(s[tt][j0 + 4], s[tt][j0 + 5]), pack_f16x2(s[tt][j0 + 6], s[tt][j0 + 7])};
-        const f16x8 pk = as_f16x8(v4);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          o[u] = mfma_f16_32x32x16(as_f16x8(ld16(vhad + 32 * kRow16 * u + 16 * cc)), pk, o[u]);
-      }
+      for (int u = 0; u < 4; ++u)
+        o[u] = mfma_f16_32x32x16(as_f16x8(ld16(vhad + 32 * kRow16 * u + 16 * cc)), pk, o[u]);
     }
   };
 
@@ -1162,10 +1099,299 @@ __device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTabl
   store_staged<256>(Vh, (__bf16 *)a.out + (qtok0 * a.Hq + w.h) * kHeadDim, a.Hq, tid);
 }
 
+// e4m3 weights: four waves of 32 queries each, three workgroups per CU.  A
+// block's S^T is computed, turned into weights and multiplied into O one
+// 64-key half at a time, so only 32 logits per lane are live and a wave fits
+// in 168 registers (three waves per SIMD).  A half that is heavy for any
+// query of the wave (heavy_block), and every half of the diagonal block, gets
+// a second e4m3 P.V pass with the rounding residual of its weights
+// (pack_lo_fp8x4): its weights then carry about 2^-8 relative error instead
+// of 2^-4.  On spread-out attention this is the first few blocks of a row at
+// most; on concentrated attention it is the blocks that hold the row's
+// weight.  V^T is held in LDS as its two key halves, each [128 d][64 keys]
+// with 80-byte rows, so that one half can be loaded while the other is in
+// use.  Per block J: barrier (K and V^T half 0 of J landed), load V^T half 1
+// of J; half 0: Q.K^T, softmax, P.V; Q.K^T of half 1; barrier (V^T half 1
+// landed, every wave done with K and V^T half 0), load K and V^T half 0 of
+// the next block; softmax and P.V of half 1.  The k and v scales of the next
+// block are read by scalar loads one step ahead.
+constexpr int kRowV = 80;                       // bytes of one d row of a V^T half in LDS
+constexpr int kHalfV8 = kHeadDim * kRowV;       // 10240 bytes
+template <bool kSparse, typename Claim>
+__device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTable &t, int rows, int item,
+                                               Claim &&claim) {
+  __shared__ __attribute__((aligned(1024))) uint8_t Ks[kTile8];       // e4m3 K, [key][d], padded rows
+  __shared__ __attribute__((aligned(1024))) uint8_t Vs[2 * kHalfV8];  // e4m3 V^T halves
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lg = lane >> 5, l32 = lane & 31;
+  const AttnItem w = decode_item(a, t, rows, item);
+  const uint8_t *kp = (const uint8_t *)a.k;
+  const int zrow = t.row[w.z];
+  const size_t ztok = (size_t)t.tok[w.z];
+  const size_t qtok0 = ztok + (size_t)w.I * kBlock;
+  const int qloc = wave * 32 + l32;
+  const size_t qtok = qtok0 + qloc;
+  cint32 *list = kSparse ? as_const(a.idx) + ((size_t)w.h * a.R + w.r) * a.k_cap : nullptr;
+  int n_blk = kSparse ? as_const(a.cnt)[(size_t)w.h * a.R + w.r] : w.I + 1;
+  if (kSparse && n_blk > a.k_cap) n_blk = a.k_cap;
+  __bf16 *orow = (__bf16 *)a.out + (qtok * a.Hq + w.h) * kHeadDim;
+  float *lse = a.lse ? a.lse + (size_t)w.h * a.T + qtok : nullptr;
+  if (n_blk <= 0) {
+    write_empty(orow, lse, lg);
+    block_sync();
+    claim();
+    block_sync();
+    return;
+  }
+  auto clampJ = [&](int x) { return x < 0 ? 0 : (x > w.I ? w.I : x); };
+  cint32 *ptab = a.table ? as_const(a.table) + (size_t)(t.z0 + w.z) * a.table_stride : nullptr;
+  auto srow = [&](int J) {
+    if (!ptab) return zrow + J;
+    const int pg = ptab[J];
+    return pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg);
+  };
+
+  i32x8 qf[2];
+  {
+    const uint8_t *qrow = (const uint8_t *)a.q + (qtok * a.Hq + w.h) * kHeadDim + 32 * lg;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 lo = ld16(qrow + 64 * ks), hi = ld16(qrow + 64 * ks + 16);
+      qf[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+  }
+  const float cq = a.q_scale[(size_t)w.r * a.Hq + w.h] * a.scale_log2;
+
+  // K tile: 1152 chunks of 16 bytes ([key][9 chunks], the ninth is padding),
+  // one chunk per lane and instruction, waves 0-1 five instructions, 2-3 four.
+  // V^T half: 640 chunks ([d][5 chunks], the fifth padding) from the image's
+  // [d][9 chunks] rows, waves 0-1 three instructions, 2-3 two.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int nk8 = wv < 2 ? 5 : 4, nv8 = wv < 2 ? 3 : 2;
+  const uint32_t kstride = (uint32_t)a.Hkv * kHeadDim;
+  uint32_t koff[5], voff[3];
+#pragma unroll
+  for (int m = 0; m < 5; ++m) {
+    const uint32_t sl = 64 * (wv + 4 * m) + lane;
+    const uint32_t r = sl / 9, ch = sl - 9 * r;
+    koff[m] = r * kstride + 16 * (ch < 8 ? ch : 0);
+  }
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    const uint32_t sl = 64 * (wv + 4 * m) + lane;
+    const uint32_t r = sl / 5, ch = sl - 5 * r;
+    voff[m] = r * kRow8 + 16 * (ch < 4 ? ch : 0);
+  }
+  const uint8_t *kbase = kp + (size_t)w.g * kHeadDim;
+  const uint8_t *v8base = a.vimg8 + ((size_t)w.g * a.R + zrow) * kTile8;
+  // buffer descriptors over one block (uniform, in SGPRs) take the per-lane
+  // offsets as 32-bit values
+  auto issue_k = [&](int J) __attribute__((always_inline)) {
+    const int pg = __builtin_amdgcn_readfirstlane(srow(J));
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(kbase + (size_t)pg * kBlock * kstride), (short)0, (int)(kBlock * kstride), kBufWord3);
+#pragma unroll
+    for (int m = 0; m < 5; ++m)
+      if (m < nk8) __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(Ks + (wv + 4 * m) * 1024), 16, koff[m], 0, 0, 0);
+  };
+  auto issue_vh = [&](int J, int hh) __attribute__((always_inline)) {
+    J = __builtin_amdgcn_readfirstlane(J);
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(v8base + (size_t)J * kTile8 + 64 * hh), (short)0, kTile8 - 64 * hh, kBufWord3);
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+      if (m < nv8)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_ptr(Vs + hh * kHalfV8 + (wv + 4 * m) * 1024), 16, voff[m], 0,
+                                                 0, 0);
+  };
+  const int krow = l32 * kRow8 + 32 * lg, vrow = l32 * kRowV + 32 * lg;
+  auto ld32 = [](const uint8_t *p) __attribute__((always_inline)) {
+    const u32x4 lo = ld16(p), hi = ld16(p + 16);
+    return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  };
+
+  // lanes l and l ^ 32 hold the two key groups of one query: v_permlane32_swap
+  // pairs them without an LDS round trip; both lanes get the same result
+  auto pair_max = [](float x) __attribute__((always_inline)) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  };
+  auto pair_sum = [](float x) __attribute__((always_inline)) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  };
+
+  float R = -INFINITY, L = 0.f;      // reference and weight sum, as in softmax_fp8
+  f32x16 o[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) o[u] = f32x16{};
+
+  typedef const __attribute__((address_space(4))) float cfloat;
+  cfloat *ksc_c = (cfloat *)a.k_scale + (size_t)zrow * a.Hkv + w.g;
+  cfloat *vsc_c = (cfloat *)a.v_scale + (size_t)zrow * a.Hkv + w.g;
+  float ksc, vsc;
+
+  // S^T of half h (keys 64 h .. 64 h + 63) for this wave's 32 queries
+  auto qk = [&](int h, f32x16 (&s)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa) {
+      s[aa] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        s[aa] = mfma_fp8_32x32x64(ld32(Ks + krow + 32 * kRow8 * (2 * h + aa) + 64 * ks), qf[ks], s[aa]);
+      __builtin_amdgcn_sched_barrier(0);   // one tile's operands in registers at a time
+    }
+  };
+  // softmax of half h and its P.V (plus the residual pass when heavy)
+  auto sm_pv = [&](auto kDiag, int h, f32x16 (&s)[2], float c, float lv, float inv_vs)
+                   __attribute__((always_inline)) {
+    constexpr bool diag = decltype(kDiag)::value;
+    if constexpr (diag) {
+      const int lim = qloc - 4 * lg - 64 * h;   // key > qloc  <=>  (key - 64 h - 4 lg) > lim
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          s[aa][i] = (32 * aa + 8 * (i >> 2) + (i & 3) > lim) ? -INFINITY : s[aa][i];
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[aa][i]);
+    // in the diagonal block a query may see no key of half 1 (cm = -inf: its
+    // weights there are 0); it always sees key 0 of half 0, so R is finite
+    // from a row's first half on
+    const float cm = pair_max(mx) * c;
+    const float mz = cm + lv;
+    if (__any(mz > R + kFp8Lazy)) {
+      const float Rn = fmaxf(R, mz);
+      const float f = __builtin_amdgcn_exp2f(R - Rn);   // 0 on the first half (R = -inf), else <= 1
+      R = Rn;
+      L *= f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[u][i] *= f;
+    }
+    const float off = lv - R + kFp8Off;
+    float psum = 0.f;
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[aa][i], c, off));
+        s[aa][i] = p;
+        psum += p;
+      }
+    L = fmaf(psum, inv_vs, L);
+    i32x8 pk;
+#pragma unroll
+    for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        pk[4 * aa + j] = (int)pack_fp8x4(s[aa][4 * j + 0], s[aa][4 * j + 1], s[aa][4 * j + 2], s[aa][4 * j + 3]);
+    // the residual (when heavy) is packed before the P.V so that the
+    // logits are dead during it
+    const bool heavy = diag || __any(heavy_block(cm, R, pair_sum(L)));
+    i32x8 pl;
+    if (heavy) {
+#pragma unroll
+      for (int aa = 0; aa < 2; ++aa)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          pl[4 * aa + j] =
+              (int)pack_lo_fp8x4(s[aa][4 * j + 0], s[aa][4 * j + 1], s[aa][4 * j + 2], s[aa][4 * j + 3]);
+    }
+    const uint8_t *vh = Vs + h * kHalfV8 + vrow;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) o[u] = mfma_fp8_32x32x64_bs(ld32(vh + 32 * kRowV * u), pk, o[u], 127);
+    if (heavy) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) o[u] = mfma_fp8_32x32x64_bs(ld32(vh + 32 * kRowV * u), pl, o[u], 127);
+    }
+  };
+
+  auto step = [&](auto kDiag, int J, int Jn, bool has_next) __attribute__((always_inline)) {
+    wait_vmcnt<0>();
+    block_sync();                    // K and V^T half 0 of J have landed; every wave is done with V^T half 1
+    issue_vh(J, 1);
+    const float c = cq * ksc;
+    // a zero V scale (an all-zero block) is taken as 2^-64, as in attn_fp8_pv16_item
+    const float vs = fmaxf(vsc, 0x1p-64f);
+    const float lv = __builtin_amdgcn_logf(vs), inv_vs = __builtin_amdgcn_rcpf(vs);
+    if (has_next) {
+      ksc = ksc_c[(size_t)Jn * a.Hkv];
+      vsc = vsc_c[(size_t)Jn * a.Hkv];
+    }
+    f32x16 s[2];
+    qk(0, s);
+    sm_pv(kDiag, 0, s, c, lv, inv_vs);
+    qk(1, s);
+    wait_vmcnt<0>();
+    block_sync();                    // V^T half 1 of J has landed; every wave is done with K and V^T half 0
+    if (has_next) {
+      issue_k(Jn);
+      issue_vh(Jn, 0);
+    }
+    sm_pv(kDiag, 1, s, c, lv, inv_vs);
+  };
+
+  int J = kSparse ? clampJ(list[0]) : 0;
+  issue_k(J);
+  issue_vh(J, 0);
+  ksc = ksc_c[(size_t)J * a.Hkv];
+  vsc = vsc_c[(size_t)J * a.Hkv];
+  const int last = kSparse ? clampJ(list[n_blk - 1]) : w.I;
+  const int n_loop = last == w.I ? n_blk - 1 : n_blk;
+  using NotDiag = std::integral_constant<bool, false>;
+  using Diag = std::integral_constant<bool, true>;
+  for (int b = 0; b < n_loop; ++b) {
+    const bool has_next = b + 1 < n_blk;
+    const int Jn = has_next ? (kSparse ? clampJ(list[b + 1]) : b + 1) : 0;
+    step(NotDiag{}, J, Jn, has_next);
+    J = Jn;
+  }
+  if (n_loop < n_blk) step(Diag{}, J, 0, false);
+
+  const float l_tot = pair_sum(L);
+  const float inv = 1.f / l_tot;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[u][i] *= inv;
+  block_sync();                      // every wave's last P.V has read Vs
+  claim();
+  // output staging: rows 0-63 in Ks, 64-127 in Vs (64 rows of 272 bytes fit
+  // in each).  The lane index is taken afresh here so that the addresses
+  // below are not computed before the item loop and held in registers
+  // through it.
+  int tid_o = tid;
+  asm volatile("" : "+v"(tid_o));
+  const int lane_o = tid_o & 63, qloc_o = (tid_o >> 6) * 32 + (lane_o & 31);
+  uint16_t *stg = (uint16_t *)(wave < 2 ? Ks : Vs) - (wave < 2 ? 0 : 64 * kOutRow);
+  stage_out(stg, o, qloc_o, lane_o >> 5);
+  if (lse && lg == 0) *lse = (R - kFp8Off + __log2f(l_tot)) * 0.69314718055994531f;
+  block_sync();
+#pragma unroll
+  for (int it = 0; it < kBlock * 16 / 256; ++it) {
+    const int cidx = it * 256 + tid_o, row = cidx >> 4, ch = cidx & 15;
+    const uint16_t *src = (const uint16_t *)(row < 64 ? Ks : Vs) + (row & 63) * kOutRow + 8 * ch;
+    st16((__bf16 *)a.out + ((qtok0 + row) * a.Hq + w.h) * kHeadDim + 8 * ch, ld16(src));
+  }
+  block_sync();                      // the next item's first loads overwrite the staging
+}
+
+template <bool kSparse>
+__global__ __launch_bounds__(256, 3) void attn_fp8_kernel(AttnLaunch a, SeqTable t, int rows, int32_t *ctr) {
+  run_items(rows * a.Hq, ctr, [&](int i, auto &&claim) { attn_fp8_item<kSparse>(a, t, rows, i, claim); });
+}
+
 // Persistent like the bf16 kernel (run_items), two workgroups per CU.
-template <bool kSparse, bool kPV16>
-__global__ __launch_bounds__(256, 2) void attn_fp8_kernel(AttnLaunch a, SeqTable t, int rows, int32_t *ctr) {
-  run_items(rows * a.Hq, ctr, [&](int i, auto &&claim) { attn_fp8_item<kSparse, kPV16>(a, t, rows, i, claim); });
+template <bool kSparse>
+__global__ __launch_bounds__(256, 2) void attn_fp8_pv16_kernel(AttnLaunch a, SeqTable t, int rows, int32_t *ctr) {
+  run_items(rows * a.Hq, ctr, [&](int i, auto &&claim) { attn_fp8_pv16_item<kSparse>(a, t, rows, i, claim); });
 }
 
 // ================================================================ launchers
@@ -1221,11 +1447,15 @@ hipError_t launch_attn(const AttnLaunch &a, const SeqTable &t, int rows, bool sp
                        int launch_index, hipStream_t s) {
   int32_t *ctr = a.ctr + 8 * launch_index;
   if (fp8) {
-    const dim3 pgrid(persistent_grid(s, rows * a.Hq, 2));
-    if (pv16 && sparse) hipLaunchKernelGGL((attn_fp8_kernel<true, true>), pgrid, dim3(256), 0, s, a, t, rows, ctr);
-    else if (pv16) hipLaunchKernelGGL((attn_fp8_kernel<false, true>), pgrid, dim3(256), 0, s, a, t, rows, ctr);
-    else if (sparse) hipLaunchKernelGGL((attn_fp8_kernel<true, false>), pgrid, dim3(256), 0, s, a, t, rows, ctr);
-    else hipLaunchKernelGGL((attn_fp8_kernel<false, false>), pgrid, dim3(256), 0, s, a, t, rows, ctr);
+    if (pv16) {
+      const dim3 pgrid(persistent_grid(s, rows * a.Hq, 2));
+      if (sparse) hipLaunchKernelGGL((attn_fp8_pv16_kernel<true>), pgrid, dim3(256), 0, s, a, t, rows, ctr);
+      else hipLaunchKernelGGL((attn_fp8_pv16_kernel<false>), pgrid, dim3(256), 0, s, a, t, rows, ctr);
+    } else {
+      const dim3 pgrid(persistent_grid(s, rows * a.Hq, 3));
+      if (sparse) hipLaunchKernelGGL((attn_fp8_kernel<true>), pgrid, dim3(256), 0, s, a, t, rows, ctr);
+      else hipLaunchKernelGGL((attn_fp8_kernel<false>), pgrid, dim3(256), 0, s, a, t, rows, ctr);
+    }
   } else {
     const dim3 pgrid(persistent_grid(s, rows * a.Hq, 1));
     if (sparse) hipLaunchKernelGGL((attn_bf16_kernel<true, false>), pgrid, dim3(512), 0, s, a, t, rows, ctr);

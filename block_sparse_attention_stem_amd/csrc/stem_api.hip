@@ -337,8 +337,9 @@ static int attn_common(const stem_problem_t *p, int32_t dtype, const void *q, co
   a.out = out;
   a.lse = lse;
   if (fp8) {
+    // the fp16 V^T image is read only with fp16 weights; the pre-pass skips it otherwise
     a.vimg8 = (uint8_t *)workspace;
-    a.vimg16 = (uint16_t *)((uint8_t *)workspace + attn_workspace_img16_offset(s.Hkv, s.R));
+    a.vimg16 = pv16 ? (uint16_t *)((uint8_t *)workspace + attn_workspace_img16_offset(s.Hkv, s.R)) : nullptr;
   } else {
     a.vimg8 = nullptr;
     a.vimg16 = (uint16_t *)workspace;
