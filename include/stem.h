@@ -190,8 +190,9 @@ int32_t stem_max_kept(const stem_problem_t *p, const double *k_start_host, doubl
  * least this many bytes, 256-byte aligned (0 for an invalid problem or
  * dtype).  Each call first rewrites it with V in the tile layout the
  * attention kernel loads (per KV head and key block, the 128 x 128 V^T tile
- * with one 16-byte pad chunk per row; fp16 for bf16 inputs, e4m3 plus fp16
- * for fp8 inputs): T * Hkv * 272 bytes for bf16; for fp8, T * Hkv * 416
+ * with one 16-byte pad chunk per row; fp16 for bf16 inputs, e4m3 for fp8
+ * inputs, plus fp16 for FP8_E4M3_PV16): T * Hkv * 272 bytes for bf16; for
+ * fp8 (either dtype), T * Hkv * 416
  * bytes plus 8 bytes per (key block, KV head) for the row-indexed K and V
  * scales that stem_bsa_prefill_paged gathers from its pages (d = 128);
  * rounded up to 256 bytes, then the work queues of the attention kernel:
@@ -227,13 +228,13 @@ size_t stem_attn_workspace_bytes(const stem_problem_t *p, int32_t dtype);   /* F
  * copy of V for bf16 inputs (V magnitudes above 65504 saturate to +-65504:
  * such inputs are outside the bf16 contract), and to e4m3 for fp8 inputs
  * (each weight times the block's V scale, relative to a running reference
- * that keeps the largest weight between 152 and 430, below e4m3's 448),
- * except in the diagonal block, which uses fp16.  An e4m3 weight is off by up
- * to 2^-4 of itself; that averages out over many keys of similar weight but
- * not when a few keys hold a query's attention, so for every 32 queries a
- * block in which some query's largest weight exceeds 1/8 of that query's
- * weight sum so far gets a second e4m3 P.V pass with the rounding residuals
- * (about 2^-8 per weight in all).  On the synthetic workloads and on
+ * that keeps the largest weight between 152 and 430, below e4m3's 448).
+ * An e4m3 weight is off by up to 2^-4 of itself; that averages out over many
+ * keys of similar weight but not when a few keys hold a query's attention, so
+ * for every 32 queries a half block (64 keys) in which some query's largest
+ * weight exceeds 1/8 of that query's weight sum so far, and the diagonal
+ * block, get a second e4m3 P.V pass with the rounding residuals (about 2^-8
+ * per weight in all).  On the synthetic workloads and on
  * concentrated attention (logits scaled up to 8x) the fp8 output stays within
  * max-abs 6e-2 of exact attention on the dequantised inputs.
  * ------------------------------------------------------------------------- */
@@ -245,11 +246,10 @@ int stem_bsa_prefill(const stem_problem_t *p, int32_t dtype, const void *q, cons
                      void *stream);
 
 /* dtype FP8_E4M3_PV16 takes the FP8_E4M3 inputs and scales but runs every
- * block's P.V like the diagonal block's: fp16 weights against the exact fp16
- * V^T image.  The e4m3 weight rounding (relative error up to 2^-4 per weight)
+ * block's P.V with fp16 weights against an exact fp16 V^T image.  The e4m3 weight rounding (relative error up to 2^-4 per weight)
  * averages out when attention is spread over many keys, but not when a few
  * keys hold it; this dtype keeps such rows at bf16-level output error, for
- * about 1.25x the e4m3 time.  Q.K^T stays e4m3 in both: the fp8 MFMA sums its
+ * about 1.35x the e4m3 time.  Q.K^T stays e4m3 in both: the fp8 MFMA sums its
  * 64 products per step with less than fp32 precision (measured error up to
  * 2^-15 of the sum of |products| on quantised Gaussian data), which shows in
  * the LSE of very large logits.  Taken by stem_bsa_prefill and
