@@ -198,6 +198,43 @@ def test_empty_rows_between_full_ones(varlen, fp8_small):
         check_out(f64(o8), ro8, FP8_MAX_ABS, None, f"fp8 with empty rows, fp16_weights={fp16_weights}")
 
 
+@pytest.mark.parametrize("gain", [1.0, 4.0])
+def test_diagonal_block_only_lists(gain):
+    """Every row lists only its own (diagonal) block, so the causal mask inside
+    one block decides every weight and the first queries of each block see one
+    to a few keys (on the e4m3 path both 64-key halves of that block take the
+    residual pass, and the queries of the first half see no key of the
+    second).  bf16, e4m3 weights and fp16 weights against the oracle; gain
+    scales Q (peaked logits at 4)."""
+    lens = (256, 640)
+    q, k, v = make_inputs(lens, 4, 2, seed=11)
+    q = (q.float() * gain).to(q.dtype)
+    cu = S.cu_from_lengths(lens)
+    p = stem.Problem(cu, 4, 2)
+    ri = np.full((4, p.R, 1), -1, dtype=np.int32)
+    rc = np.ones((4, p.R), dtype=np.int32)
+    for z in range(len(lens)):
+        r0, r1 = cu[z] // 128, cu[z + 1] // 128
+        ri[:, r0:r1, 0] = np.arange(r1 - r0, dtype=np.int32)
+    idx, cnt = to_dev(torch.from_numpy(ri), torch.from_numpy(rc))
+    qf, kf, vf = (f64(t) for t in (q, k, v))
+    out, lse = stem.stem_bsa_prefill(p, *to_dev(q, k, v), idx, cnt, SCALE, want_lse=True)
+    ro, rl = O.block_sparse_attention(qf, kf, vf, ri, rc, cu, 4, 2, SCALE)
+    check_out(f64(out), ro, BF16_MAX_ABS, BF16_MEAN_REL, f"bf16 diagonal-only lists, gain {gain}")
+    check_lse(lse.cpu().numpy().astype(np.float64), rl, f"bf16 diagonal-only lists, gain {gain}")
+
+    (q8, k8, v8), (qs, ks, vs) = quantize_fp8(q, k, v, lens)
+    qd8, kd8, vd8 = dequant(q8, qs), dequant(k8, ks), dequant(v8, vs)
+    ro8, rl8 = O.block_sparse_attention(qd8, kd8, vd8, ri, rc, cu, 4, 2, SCALE)
+    sc = to_dev(qs, ks, vs)
+    o8, l8 = stem.stem_bsa_prefill(p, *to_dev(q8, k8, v8), idx, cnt, SCALE, scales=sc, want_lse=True)
+    check_out(f64(o8), ro8, FP8_MAX_ABS, None, f"fp8 diagonal-only lists, gain {gain}")
+    if gain == 1.0:
+        check_lse(l8.cpu().numpy().astype(np.float64), rl8, f"fp8 diagonal-only lists, gain {gain}")
+    o16 = stem.stem_bsa_prefill(p, *to_dev(q8, k8, v8), idx, cnt, SCALE, scales=sc, fp16_weights=True)
+    check_out(f64(o16), ro8, BF16_MAX_ABS, BF16_MEAN_REL, f"fp8 inputs, fp16 weights, diagonal-only lists, gain {gain}")
+
+
 def test_chunk_size_changes_no_score(varlen):
     lens, (q, k, v), _ = varlen
     p = stem.Problem(S.cu_from_lengths(lens), 4, 2)
