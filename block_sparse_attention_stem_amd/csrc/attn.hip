@@ -1383,12 +1383,13 @@ __device__ __forceinline__ void attn_fp8_item(const AttnLaunch &a, const SeqTabl
   block_sync();                      // the next item's first loads overwrite the staging
 }
 
+// Both fp8 kernels are persistent like the bf16 kernel (run_items): three
+// workgroups per CU for e4m3 weights, two for fp16 weights.
 template <bool kSparse>
 __global__ __launch_bounds__(256, 3) void attn_fp8_kernel(AttnLaunch a, SeqTable t, int rows, int32_t *ctr) {
   run_items(rows * a.Hq, ctr, [&](int i, auto &&claim) { attn_fp8_item<kSparse>(a, t, rows, i, claim); });
 }
 
-// Persistent like the bf16 kernel (run_items), two workgroups per CU.
 template <bool kSparse>
 __global__ __launch_bounds__(256, 2) void attn_fp8_pv16_kernel(AttnLaunch a, SeqTable t, int rows, int32_t *ctr) {
   run_items(rows * a.Hq, ctr, [&](int i, auto &&claim) { attn_fp8_pv16_item<kSparse>(a, t, rows, i, claim); });
